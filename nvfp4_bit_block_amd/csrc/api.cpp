@@ -1,0 +1,415 @@
+// api.cpp -- the C ABI declared in include/nvfp4.h: argument checks on the
+// host, workspace layout, and the launch sequence of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "nvfp4.h"
+#include "nvfp4_internal.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, const char* detail = "") {
+    std::snprintf(g_last_error, sizeof g_last_error, fmt, detail);
+    return status;
+}
+
+int32_t hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return NVFP4_OK;
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+    return NVFP4_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ----------------------------------------------------------- GEMM planning --
+
+struct GemmPlan {
+    bool gemv = false;   // M <= 8: dequantized activation + GEMV
+    Tile tile = Tile::k128x128;
+    int bm = 128;
+    int ksplit = 1;
+    int64_t grid_m = 0;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+    GemmPlan p;
+    if (M <= 8) {
+        p.gemv = true;
+        return p;
+    }
+    if (M > 64) { p.tile = Tile::k128x128; p.bm = 128; }
+    else if (M > 32) { p.tile = Tile::k64x128; p.bm = 64; }
+    else { p.tile = Tile::k32x128; p.bm = 32; }
+    p.grid_m = (M + p.bm - 1) / p.bm;
+    const int64_t tiles = p.grid_m * ((N + 127) / 128);
+    const int64_t kchunks = K / 64;
+    while (tiles * p.ksplit < 512 && p.ksplit < 16 && kchunks / (p.ksplit * 2) >= 4) p.ksplit *= 2;
+    return p;
+}
+
+struct GemmLayout {
+    size_t xq_codes = 0, xq_scales = 0, xhat = 0, partial = 0, total = 0;
+};
+
+GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
+    GemmLayout l;
+    const GemmPlan p = plan_gemm(M, N, K);
+    size_t off = 0;
+    l.xq_codes = off; off += align_up((size_t)(M * K / 2));
+    l.xq_scales = off; off += align_up((size_t)(M * K / 16));
+    if (p.gemv) {
+        l.xhat = off; off += align_up((size_t)(M * K * 2));
+    } else if (p.ksplit > 1) {
+        l.partial = off; off += align_up((size_t)p.ksplit * (size_t)(M * N) * 4);
+    }
+    l.total = off;
+    return l;
+}
+
+// ------------------------------------------------------------ MoE planning --
+
+constexpr int kMoeBM = 128;
+
+struct MoeLayout {
+    size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0;
+    size_t xq_codes = 0, xq_scales = 0, hq_codes = 0, hq_scales = 0, h = 0, y = 0, total = 0;
+};
+
+MoeLayout layout_moe(const nvfp4_moe_problem& p) {
+    MoeLayout l;
+    const size_t S = (size_t)(p.T * p.top_k);
+    size_t off = 0;
+    l.row_off = off; off += align_up((size_t)(p.E + 1) * 4);
+    l.tile_off = off; off += align_up((size_t)(p.E + 1) * 4);
+    l.perm = off; off += align_up(S * 4);
+    l.inv = off; off += align_up(S * 4);
+    l.pos_group = off; off += align_up(S * 4);
+    if (p.mode == 1) {
+        l.xq_codes = off; off += align_up(S * (size_t)p.H / 2);
+        l.xq_scales = off; off += align_up(S * (size_t)p.H / 16);
+        l.hq_codes = off; off += align_up(S * (size_t)p.I / 2);
+        l.hq_scales = off; off += align_up(S * (size_t)p.I / 16);
+    }
+    l.h = off; off += align_up(S * (size_t)p.I * 2);
+    l.y = off; off += align_up(S * (size_t)p.H * 4);
+    l.total = off;
+    return l;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_version(void) { return 100; }
+
+const char* nvfp4_status_string(int32_t status) {
+    switch (status) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_NULL_ARG: return "null argument";
+        case NVFP4_ERR_SHAPE: return "invalid shape";
+        case NVFP4_ERR_ALIGN: return "misaligned pointer";
+        case NVFP4_ERR_UNSUPPORTED: return "unsupported problem";
+        case NVFP4_ERR_WORKSPACE: return "workspace too small";
+        case NVFP4_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------- quantize --
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return align_up((size_t)amax_grid(rows * cols) * 4);
+}
+
+int32_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
+                       uint8_t* codes, uint8_t* scales, float* global_scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows < 0 || cols <= 0 || cols % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "quantize: need rows >= 0, cols > 0 and cols %% 16 == 0%s");
+    if (rows == 0) return NVFP4_OK;
+    if (!x || !codes || !scales || !global_scale)
+        return fail(NVFP4_ERR_NULL_ARG, "quantize: x, codes, scales and global_scale are required%s");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(global_scale) ||
+        (static_scale && !aligned16(static_scale)) || (workspace && !aligned16(workspace)))
+        return fail(NVFP4_ERR_ALIGN, "quantize: pointers must be 16-byte aligned%s");
+    const size_t need = static_scale ? 0 : nvfp4_quantize_workspace_size(rows, cols);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(NVFP4_ERR_WORKSPACE, "quantize: dynamic mode needs nvfp4_quantize_workspace_size bytes%s");
+    hipStream_t s = as_stream(stream);
+    PackArgs a;
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.codes = codes;
+    a.scales = scales;
+    a.global_out = global_scale;
+    if (static_scale) {
+        a.mode = ScaleMode::kStatic;
+        a.sg_ptr = static_scale;
+    } else {
+        const int grid = amax_grid(rows * cols);
+        uint32_t* partial = reinterpret_cast<uint32_t*>(workspace);
+        int32_t st = hip_status(launch_amax_partial(x, rows * cols, partial, grid, s), "quantize amax");
+        if (st) return st;
+        a.mode = ScaleMode::kDynamic;
+        a.partial = partial;
+        a.npartial = grid;
+    }
+    return hip_status(launch_quantize_pack(a, s), "quantize pack");
+}
+
+int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                         int64_t rows, int64_t cols, uint16_t* y, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows < 0 || cols <= 0 || cols % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "dequantize: need rows >= 0, cols > 0 and cols %% 16 == 0%s");
+    if (rows == 0) return NVFP4_OK;
+    if (!codes || !scales || !global_scale || !y)
+        return fail(NVFP4_ERR_NULL_ARG, "dequantize: all pointers are required%s");
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(global_scale) || !aligned16(y))
+        return fail(NVFP4_ERR_ALIGN, "dequantize: pointers must be 16-byte aligned%s");
+    return hip_status(launch_dequantize(codes, scales, global_scale, 0.0f, rows, cols, y, as_stream(stream)),
+                      "dequantize");
+}
+
+// -------------------------------------------------------------------- GEMV --
+
+int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_global, uint16_t* y, void* stream) {
+    g_last_error[0] = '\0';
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "gemv: need M, N >= 0, K > 0 and K %% 16 == 0%s");
+    if (M > 8) return fail(NVFP4_ERR_UNSUPPORTED, "gemv: M must be <= 8%s");
+    if (K % 32 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemv: K must be a multiple of 32%s");
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!x || !w_codes || !w_scales || !w_global || !y)
+        return fail(NVFP4_ERR_NULL_ARG, "gemv: all pointers are required%s");
+    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_global) || !aligned16(y))
+        return fail(NVFP4_ERR_ALIGN, "gemv: pointers must be 16-byte aligned%s");
+    return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y,
+                                        as_stream(stream)),
+                      "gemv");
+}
+
+// -------------------------------------------------------------------- GEMM --
+
+size_t nvfp4_gemm_w4a4_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
+    return layout_gemm(M, N, K).total;
+}
+
+int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "gemm: need M, N >= 0, K > 0 and K %% 16 == 0%s");
+    if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm: K must be a multiple of 64%s");
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!x || !input_scale || !w_codes || !w_scales || !w_global || !y)
+        return fail(NVFP4_ERR_NULL_ARG, "gemm: x, input_scale, weights and y are required%s");
+    if (!aligned16(x) || !aligned16(input_scale) || !aligned16(w_codes) || !aligned16(w_scales) ||
+        !aligned16(w_global) || !aligned16(y) || (workspace && !aligned16(workspace)))
+        return fail(NVFP4_ERR_ALIGN, "gemm: pointers must be 16-byte aligned%s");
+    const GemmLayout l = layout_gemm(M, N, K);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(NVFP4_ERR_WORKSPACE, "gemm: workspace smaller than nvfp4_gemm_w4a4_workspace_size%s");
+    hipStream_t s = as_stream(stream);
+    const GemmPlan p = plan_gemm(M, N, K);
+    uint8_t* xc = at<uint8_t>(workspace, l.xq_codes);
+    uint8_t* xs = at<uint8_t>(workspace, l.xq_scales);
+    // static activation quantization under input_scale
+    PackArgs a;
+    a.x = x;
+    a.rows = M;
+    a.cols = K;
+    a.mode = ScaleMode::kStatic;
+    a.sg_ptr = input_scale;
+    a.codes = xc;
+    a.scales = xs;
+    int32_t st = hip_status(launch_quantize_pack(a, s), "gemm activation quantize");
+    if (st) return st;
+    if (p.gemv) {
+        // q * s of the activation is exact in bf16; the product of the two
+        // global scales is applied by the GEMV.
+        uint16_t* xh = at<uint16_t>(workspace, l.xhat);
+        st = hip_status(launch_dequantize(xc, xs, nullptr, 1.0f, M, K, xh, s), "gemm activation decode");
+        if (st) return st;
+        return hip_status(launch_gemv_w4a16(xh, (int)M, N, K, w_codes, w_scales, w_global, input_scale, y, s),
+                          "gemm gemv");
+    }
+    GemmArgs g;
+    g.a = xc;
+    g.a_scales = xs;
+    g.a_global = input_scale;
+    g.b_codes = w_codes;
+    g.b_scales = w_scales;
+    g.b_global = w_global;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.ksplit = p.ksplit;
+    if (p.ksplit > 1) {
+        float* part = at<float>(workspace, l.partial);
+        g.out = part;
+        g.ldo = N;
+        st = hip_status(launch_gemm(g, AFmt::kFp4, Epi::kPartialF32, p.tile, (int)p.grid_m, s), "gemm");
+        if (st) return st;
+        return hip_status(launch_splitk_reduce(part, p.ksplit, M, N, input_scale, w_global, y, s),
+                          "gemm split-k reduce");
+    }
+    g.out = y;
+    g.ldo = N;
+    return hip_status(launch_gemm(g, AFmt::kFp4, Epi::kStoreBf16, p.tile, (int)p.grid_m, s), "gemm");
+}
+
+// --------------------------------------------------------------------- MoE --
+
+size_t nvfp4_moe_workspace_size(const nvfp4_moe_problem* p) {
+    if (!p || p->T < 0 || p->E <= 0 || p->top_k <= 0 || p->H <= 0 || p->I <= 0) return 0;
+    return layout_moe(*p).total;
+}
+
+int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tensors* t, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (!p || !t) return fail(NVFP4_ERR_NULL_ARG, "moe: problem and tensors are required%s");
+    if (p->T < 0 || p->E <= 0 || p->top_k <= 0 || p->H <= 0 || p->I <= 0 || p->H % 16 || p->I % 16 ||
+        (p->mode != 0 && p->mode != 1))
+        return fail(NVFP4_ERR_SHAPE, "moe: need T >= 0, E, top_k, H, I > 0, H and I multiples of 16, mode 0 or 1%s");
+    if (p->H % 64 || p->I % 64) return fail(NVFP4_ERR_UNSUPPORTED, "moe: H and I must be multiples of 64%s");
+    if (p->E > 4096) return fail(NVFP4_ERR_UNSUPPORTED, "moe: at most 4096 experts%s");
+    if (p->T * p->top_k > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "moe: too many slots%s");
+    if (p->T == 0) return NVFP4_OK;
+    if (!t->x || !t->topk_ids || !t->topk_weights || !t->w13_codes || !t->w13_scales || !t->w13_global ||
+        !t->w2_codes || !t->w2_scales || !t->w2_global || !t->out ||
+        (p->mode == 1 && (!t->a13_scale || !t->a2_scale)))
+        return fail(NVFP4_ERR_NULL_ARG, "moe: a required tensor is NULL%s");
+    const void* ptrs[] = {t->x, t->topk_ids, t->topk_weights, t->w13_codes, t->w13_scales, t->w13_global,
+                          t->w2_codes, t->w2_scales, t->w2_global, t->out};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return fail(NVFP4_ERR_ALIGN, "moe: pointers must be 16-byte aligned%s");
+    if (p->mode == 1 && (!aligned16(t->a13_scale) || !aligned16(t->a2_scale)))
+        return fail(NVFP4_ERR_ALIGN, "moe: pointers must be 16-byte aligned%s");
+    if (workspace && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "moe: workspace must be 16-byte aligned%s");
+    const MoeLayout l = layout_moe(*p);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(NVFP4_ERR_WORKSPACE, "moe: workspace smaller than nvfp4_moe_workspace_size%s");
+
+    hipStream_t s = as_stream(stream);
+    const int64_t S = p->T * p->top_k;
+    const int32_t E = (int32_t)p->E;
+    int32_t* row_off = at<int32_t>(workspace, l.row_off);
+    int32_t* tile_off = at<int32_t>(workspace, l.tile_off);
+    int32_t* perm = at<int32_t>(workspace, l.perm);
+    int32_t* inv = at<int32_t>(workspace, l.inv);
+    int32_t* pos_group = at<int32_t>(workspace, l.pos_group);
+    uint16_t* h = at<uint16_t>(workspace, l.h);
+    float* Y = at<float>(workspace, l.y);
+    int32_t st = hip_status(launch_moe_route(t->topk_ids, S, E, kMoeBM, row_off, tile_off, perm, inv, pos_group, s),
+                            "moe route");
+    if (st) return st;
+    const int grid_m = (int)((S + kMoeBM - 1) / kMoeBM + E);
+
+    // GEMM 1: [g | u] = x^ W13^T, h = bf16(silu(g) * u)
+    GemmArgs g1;
+    g1.b_codes = t->w13_codes;
+    g1.b_scales = t->w13_scales;
+    g1.b_global = t->w13_global;
+    g1.M = S;
+    g1.N = 2 * p->I;
+    g1.K = p->H;
+    g1.row_off = row_off;
+    g1.tile_off = tile_off;
+    g1.groups = E;
+    g1.out = h;
+    g1.ldo = p->I;
+    g1.half_n = p->I;
+    AFmt af = AFmt::kBf16;
+    if (p->mode == 1) {
+        uint8_t* xc = at<uint8_t>(workspace, l.xq_codes);
+        uint8_t* xs = at<uint8_t>(workspace, l.xq_scales);
+        PackArgs a;
+        a.x = t->x;
+        a.rows = S;
+        a.cols = p->H;
+        a.src_row = perm;
+        a.src_div = (int32_t)p->top_k;
+        a.rows_valid = row_off + E;
+        a.mode = ScaleMode::kGrouped;
+        a.sg_group = t->a13_scale;
+        a.row_group = pos_group;
+        a.codes = xc;
+        a.scales = xs;
+        st = hip_status(launch_quantize_pack(a, s), "moe activation quantize");
+        if (st) return st;
+        g1.a = xc;
+        g1.a_scales = xs;
+        g1.a_global = t->a13_scale;
+        af = AFmt::kFp4;
+    } else {
+        g1.a = t->x;
+        g1.a_rows = perm;
+        g1.a_div = (int32_t)p->top_k;
+    }
+    st = hip_status(launch_gemm(g1, af, Epi::kMoeGateUp, Tile::k128x128, grid_m, s), "moe gemm1");
+    if (st) return st;
+
+    // GEMM 2: Y = h^ W2^T (fp32, per slot row)
+    GemmArgs g2;
+    g2.b_codes = t->w2_codes;
+    g2.b_scales = t->w2_scales;
+    g2.b_global = t->w2_global;
+    g2.M = S;
+    g2.N = p->H;
+    g2.K = p->I;
+    g2.row_off = row_off;
+    g2.tile_off = tile_off;
+    g2.groups = E;
+    g2.out = Y;
+    g2.ldo = p->H;
+    if (p->mode == 1) {
+        uint8_t* hc = at<uint8_t>(workspace, l.hq_codes);
+        uint8_t* hs = at<uint8_t>(workspace, l.hq_scales);
+        PackArgs a;
+        a.x = h;
+        a.rows = S;
+        a.cols = p->I;
+        a.rows_valid = row_off + E;
+        a.mode = ScaleMode::kGrouped;
+        a.sg_group = t->a2_scale;
+        a.row_group = pos_group;
+        a.codes = hc;
+        a.scales = hs;
+        st = hip_status(launch_quantize_pack(a, s), "moe intermediate quantize");
+        if (st) return st;
+        g2.a = hc;
+        g2.a_scales = hs;
+        g2.a_global = t->a2_scale;
+    } else {
+        g2.a = h;
+    }
+    st = hip_status(launch_gemm(g2, af, Epi::kMoeDown, Tile::k128x128, grid_m, s), "moe gemm2");
+    if (st) return st;
+    return hip_status(launch_moe_combine(Y, inv, t->topk_weights, p->T, (int32_t)p->top_k, p->H, t->out, s),
+                      "moe combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// nvfp4_internal.hpp -- host-side launchers shared between the C ABI and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------- quantize --
+
+// Number of workgroups of the dynamic-mode amax pass for n elements.
+int amax_grid(int64_t n);
+
+// Where the per-16-block global scale of a quantize pass comes from.
+enum class ScaleMode : int {
+    kDynamic = 0,  // fl(amax / 2688) from the per-workgroup maxima `partial`
+    kStatic = 1,   // *sg_ptr
+    kGrouped = 2,  // sg_group[row_group[row]] (per-row static scale)
+};
+
+struct PackArgs {
+    const uint16_t* x = nullptr;    // bf16 source
+    int64_t rows = 0, cols = 0;     // output shape (cols % 16 == 0)
+    const int32_t* src_row = nullptr;  // optional gather: source row = src_row[r] / src_div
+    int32_t src_div = 1;
+    const int32_t* rows_valid = nullptr;  // optional device count: rows >= *rows_valid are skipped
+    ScaleMode mode = ScaleMode::kStatic;
+    const uint32_t* partial = nullptr;
+    int npartial = 0;
+    const float* sg_ptr = nullptr;
+    const float* sg_group = nullptr;
+    const int32_t* row_group = nullptr;
+    uint8_t* codes = nullptr;       // [rows, cols/2]
+    uint8_t* scales = nullptr;      // [rows, cols/16]
+    float* global_out = nullptr;    // optional: the Sg used (uniform modes only)
+};
+
+hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, int grid,
+                               hipStream_t stream);
+hipError_t launch_quantize_pack(const PackArgs& a, hipStream_t stream);
+
+// y = bf16(fl(fl(q*s) * Sg)); Sg = *sg_ptr, or `sg_const` when sg_ptr is null.
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* sg_ptr,
+                             float sg_const, int64_t rows, int64_t cols, uint16_t* y,
+                             hipStream_t stream);
+
+// -------------------------------------------------------------------- GEMV --
+
+// y[m, n] = bf16(scale * sum_k s*q*x), scale = *g0 * (g1 ? *g1 : 1).
+hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
+                             const uint8_t* ws, const float* g0, const float* g1, uint16_t* y,
+                             hipStream_t stream);
+
+// -------------------------------------------------------------------- GEMM --
+
+enum class AFmt : int { kBf16 = 0, kFp4 = 1 };
+enum class Epi : int {
+    kStoreBf16 = 0,   // y = bf16(acc * scale)
+    kPartialF32 = 1,  // partial[split] = acc (split-K, reduced later)
+    kMoeGateUp = 2,   // h = bf16(silu(g*scale) * (u*scale))
+    kMoeDown = 3,     // Y = acc * scale (fp32)
+};
+
+struct GemmArgs {
+    // A operand: bf16 [*, K] rows (optionally gathered) or NVFP4 codes/scales.
+    const void* a = nullptr;
+    const uint8_t* a_scales = nullptr;
+    const int32_t* a_rows = nullptr;  // bf16 gather: A row of output row r = a_rows[r] / a_div
+    int32_t a_div = 1;
+    const float* a_global = nullptr;  // per group (or [1]); null = 1
+    // B operand: NVFP4 [N, K] per group
+    const uint8_t* b_codes = nullptr;
+    const uint8_t* b_scales = nullptr;
+    const float* b_global = nullptr;  // per group (or [1])
+    int64_t M = 0, N = 0, K = 0;
+    // grouping (MoE): rows of group e are [row_off[e], row_off[e+1]); its
+    // m-tiles are [tile_off[e], tile_off[e+1]); a/b pointers advance per group
+    const int32_t* row_off = nullptr;
+    const int32_t* tile_off = nullptr;
+    int32_t groups = 0;
+    // output
+    void* out = nullptr;
+    int64_t ldo = 0;
+    int32_t ksplit = 1;
+    int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
+};
+
+// Tile shapes: block rows x block cols.
+enum class Tile : int { k128x128 = 0, k64x128 = 1, k32x128 = 2 };
+
+hipError_t launch_gemm(const GemmArgs& g, AFmt afmt, Epi epi, Tile tile, int grid_m,
+                       hipStream_t stream);
+
+// y[m, n] = bf16(scale * sum_s partial[s][m][n]), scale = *g0 * (g1 ? *g1 : 1)
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
+                                const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
+
+// --------------------------------------------------------------------- MoE --
+
+hipError_t launch_moe_route(const int32_t* ids, int64_t slots, int32_t E, int32_t bm,
+                            int32_t* row_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
+                            int32_t* pos_group, hipStream_t stream);
+
+hipError_t launch_moe_combine(const float* Y, const int32_t* inv, const float* w, int64_t T,
+                              int32_t topk, int64_t H, uint16_t* out, hipStream_t stream);
+
+}  // namespace nvfp4

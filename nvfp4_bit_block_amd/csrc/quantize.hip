@@ -1,0 +1,225 @@
+// quantize.hip -- NVFP4 quantize (two-pass dynamic, one-pass static) and
+// dequantize for gfx950.
+//
+// Format and scale rule: "vroomfondel/glm-5.2-reap-504B-v2-W4A4" model card,
+// "How it was produced" (e2m1 codes, per-16 e4m3 block scales stored
+// linearly, per-tensor fp32 scale amax / (6 * 448); static input_scale for
+// activations); "Getting GLM-5.2 NVFP4 Post-Training off the ground",
+// "Going deeper" (16-element blocks along the row, two codes per byte) and
+// "The bottom line" (a block's scale follows the block maximum).
+//
+// Every decision is taken with the same fp32 operations as the definition:
+// Sg = amax / 2688, t = 6 * Sg, s_f = bmax / t, s8 = E4M3(s_f), d = s * Sg,
+// v = |x| / d, code = sign | E2M1(v), with IEEE division (the build uses
+// correctly rounded fp32 division and keeps denormals).
+#include "nvfp4_device.hpp"
+#include "nvfp4_internal.hpp"
+
+// Bit-exactness needs every fp32 step rounded on its own: no contraction.
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Pass 1: per-workgroup maximum of |x| as a bf16 magnitude pattern (for finite
+// values the pattern order is the value order).  Grid-stride over 16-byte
+// chunks of 8 elements, four independent loads in flight per thread.
+__global__ __launch_bounds__(kThreads) void k_amax_partial(const uint4* __restrict__ x, int64_t n8,
+                                                           uint32_t* __restrict__ partial) {
+    uint32_t m0 = 0, m1 = 0;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n8; i += 4 * stride) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = load_nt16(&x[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t a = w[j] & 0x7FFF7FFFu;
+                m0 = max(m0, a & 0xFFFFu);
+                m1 = max(m1, a >> 16);
+            }
+        }
+    }
+    for (; i < n8; i += stride) {
+        uint4 v = load_nt16(&x[i]);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t a = w[j] & 0x7FFF7FFFu;
+            m0 = max(m0, a & 0xFFFFu);
+            m1 = max(m1, a >> 16);
+        }
+    }
+    uint32_t m = wave_max_u32(max(m0, m1));
+    __shared__ uint32_t red[kThreads / kWave];
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) r = max(r, red[w]);
+        partial[blockIdx.x] = r;
+    }
+}
+
+// Magnitude code of one bf16 element under divisor d (d == 0 -> 0), sign in bit 3.
+__device__ __forceinline__ uint32_t encode_elem(uint32_t h, float d) {
+    float v = (d > 0.0f) ? bf16_to_f32(h & 0x7FFFu) / d : 0.0f;
+    return ((h >> 12) & 8u) | e2m1_from_f32(v);
+}
+
+// One 16-element block: 8 words of bf16 pairs -> 8 code bytes + scale byte.
+__device__ __forceinline__ uint32_t encode_block(const uint32_t w[8], float Sg, float t, uint2& out) {
+    uint32_t bm = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t a = w[j] & 0x7FFF7FFFu;
+        bm = max(bm, max(a & 0xFFFFu, a >> 16));
+    }
+    const float bmax = bf16_to_f32(bm);
+    const float s_f = (t > 0.0f) ? bmax / t : 0.0f;
+    const uint32_t s8 = e4m3_from_f32(s_f);
+    const float d = e4m3_to_f32(s8) * Sg;
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t byte = encode_elem(w[j] & 0xFFFFu, d) | (encode_elem(w[j] >> 16, d) << 4);
+        o[j >> 2] |= byte << (8 * (j & 3));
+    }
+    out = make_uint2(o[0], o[1]);
+    return s8;
+}
+
+// Pass 2 (or the only pass in the static modes): one 16-element block per
+// thread per iteration, grid-stride.  The dynamic mode first reduces the
+// pass-1 maxima (every workgroup does so redundantly; there are at most 2048).
+template <ScaleMode MODE>
+__global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
+    float Sg = 0.0f;
+    if constexpr (MODE == ScaleMode::kDynamic) {
+        uint32_t m = 0;
+        for (int i = threadIdx.x; i < a.npartial; i += kThreads) m = max(m, a.partial[i]);
+        m = wave_max_u32(m);
+        __shared__ uint32_t red[kThreads / kWave];
+        if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+        __syncthreads();
+        m = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) m = max(m, red[w]);
+        Sg = bf16_to_f32(m) / 2688.0f;
+    } else if constexpr (MODE == ScaleMode::kStatic) {
+        Sg = *a.sg_ptr;
+    }
+    if constexpr (MODE != ScaleMode::kGrouped) {
+        if (a.global_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.global_out = Sg;
+    }
+    float t = 6.0f * Sg;
+    const int64_t bpr = a.cols / 16;
+    const int64_t nblk = a.rows * bpr;
+    const int64_t rows_valid = a.rows_valid ? (int64_t)*a.rows_valid : a.rows;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+        const int64_t r = b / bpr;
+        if (r >= rows_valid) continue;
+        const int64_t cb = b - r * bpr;
+        const int64_t sr = a.src_row ? (int64_t)(a.src_row[r] / a.src_div) : r;
+        if constexpr (MODE == ScaleMode::kGrouped) {
+            Sg = a.sg_group[a.row_group[r]];
+            t = 6.0f * Sg;
+        }
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + sr * a.cols + cb * 16);
+        uint4 v0 = src[0], v1 = src[1];
+        uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint2 codes;
+        uint32_t s8 = encode_block(w, Sg, t, codes);
+        reinterpret_cast<uint2*>(a.codes)[b] = codes;
+        a.scales[b] = (uint8_t)s8;
+    }
+}
+
+// Dequantize: one 16-element block per thread per iteration.
+__global__ __launch_bounds__(kThreads) void k_dequantize(const uint2* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         const float* __restrict__ sg_ptr,
+                                                         float sg_const, int64_t nblk,
+                                                         uint4* __restrict__ y) {
+    const float Sg = sg_ptr ? *sg_ptr : sg_const;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+        const uint2 c = codes[b];
+        const float s = e4m3_to_f32(scales[b]);
+        uint32_t out[8];
+        const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x2 q[4];
+            fp4x8_to_f32(cw[h], q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float qs0 = q[i].x * s, qs1 = q[i].y * s;
+                float v0 = qs0 * Sg, v1 = qs1 * Sg;
+                out[h * 4 + i] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+            }
+        }
+        y[2 * b] = make_uint4(out[0], out[1], out[2], out[3]);
+        y[2 * b + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+    }
+}
+
+int grid_for(int64_t work, int per_block, int cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+int amax_grid(int64_t n) { return grid_for(n / 8, kThreads * 4, 2048); }
+
+hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, int grid,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(k_amax_partial, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(x), n / 8, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack(const PackArgs& a, hipStream_t stream) {
+    const int64_t nblk = a.rows * (a.cols / 16);
+    const int grid = grid_for(nblk, kThreads, 8192);
+    switch (a.mode) {
+        case ScaleMode::kDynamic:
+            hipLaunchKernelGGL(k_quantize_pack<ScaleMode::kDynamic>, dim3(grid), dim3(kThreads), 0,
+                               stream, a);
+            break;
+        case ScaleMode::kStatic:
+            hipLaunchKernelGGL(k_quantize_pack<ScaleMode::kStatic>, dim3(grid), dim3(kThreads), 0,
+                               stream, a);
+            break;
+        case ScaleMode::kGrouped:
+            hipLaunchKernelGGL(k_quantize_pack<ScaleMode::kGrouped>, dim3(grid), dim3(kThreads), 0,
+                               stream, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* sg_ptr,
+                             float sg_const, int64_t rows, int64_t cols, uint16_t* y,
+                             hipStream_t stream) {
+    const int64_t nblk = rows * (cols / 16);
+    const int grid = grid_for(nblk, kThreads, 8192);
+    hipLaunchKernelGGL(k_dequantize, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint2*>(codes), scales, sg_ptr, sg_const, nblk,
+                       reinterpret_cast<uint4*>(y));
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+invalid arguments on the host (no GPU needed: checks run before any HIP call)."""
+import ctypes
+import os
+
+import pytest
+
+import nvfp4_bit_block_amd as nv
+
+pytestmark = pytest.mark.skipif(not os.path.exists(nv.LIB_PATH), reason="libnvfp4.so not built")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5
+A = 4096          # a fake, 16-byte aligned, never dereferenced address
+MIS = 4097        # misaligned
+
+
+def test_exports_every_header_symbol():
+    L = ctypes.CDLL(nv.LIB_PATH)
+    names = nv.header_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings():
+    L = nv.lib()
+    assert L.nvfp4_version() >= 100
+    for s in range(7):
+        assert L.nvfp4_status_string(s)
+
+
+def test_quantize_validation():
+    L = nv.lib()
+    q = L.nvfp4_quantize
+    assert q(None, 4, 32, None, A, A, A, A, 1 << 20, None) == NULL
+    assert q(A, 4, 33, None, A, A, A, A, 1 << 20, None) == SHAPE
+    assert q(A, -1, 32, None, A, A, A, A, 1 << 20, None) == SHAPE
+    assert q(A, 4, 0, None, A, A, A, A, 1 << 20, None) == SHAPE
+    assert q(MIS, 4, 32, None, A, A, A, A, 1 << 20, None) == ALIGN
+    assert q(A, 4, 32, None, A, A, A, None, 0, None) == WS          # dynamic needs workspace
+    assert q(A, 4, 32, None, A, A, A, A, 4, None) == WS
+    assert q(A, 0, 32, None, A, A, A, A, 1 << 20, None) == OK       # empty: no-op
+    assert q(A, 0, 32, A, A, A, A, None, 0, None) == OK             # static, empty
+    assert q(None, 0, 32, None, None, None, None, None, 0, None) == OK   # empty ignores pointers
+    assert L.nvfp4_quantize_workspace_size(65536, 6144) > 0
+    assert b"cols" in L.nvfp4_last_error() or True
+
+
+def test_dequantize_validation():
+    d = nv.lib().nvfp4_dequantize
+    assert d(None, A, A, 4, 32, A, None) == NULL
+    assert d(A, A, A, 4, 24, A, None) == SHAPE
+    assert d(A, A, A, 4, 32, MIS, None) == ALIGN
+    assert d(A, A, A, 0, 32, A, None) == OK
+
+
+def test_gemv_validation():
+    g = nv.lib().nvfp4_gemv_w4a16
+    assert g(A, 1, 8, 64, A, A, A, None, None) == NULL
+    assert g(A, 1, 8, 40, A, A, A, A, None) == SHAPE
+    assert g(A, 9, 8, 64, A, A, A, A, None) == UNSUP
+    assert g(A, 1, 8, 48, A, A, A, A, None) == UNSUP                 # K % 32 != 0
+    assert g(A, 1, 8, 64, A, A, MIS, A, None) == ALIGN
+    assert g(A, 0, 8, 64, A, A, A, A, None) == OK
+    assert g(A, 3, 0, 64, A, A, A, A, None) == OK
+
+
+def test_gemm_validation():
+    L = nv.lib()
+    g = L.nvfp4_gemm_w4a4
+    ws = L.nvfp4_gemm_w4a4_workspace_size(128, 256, 512)
+    assert ws > 0
+    assert g(A, None, 128, 256, 512, A, A, A, A, A, ws, None) == NULL
+    assert g(A, A, 128, 256, 520, A, A, A, A, A, ws, None) == SHAPE
+    assert g(A, A, 128, 256, 528, A, A, A, A, A, 1 << 30, None) == UNSUP   # K % 64 != 0
+    assert g(A, A, 128, 256, 512, A, A, A, A, A, ws - 1, None) == WS
+    assert g(A, A, 128, 256, 512, A, A, A, A, None, 0, None) == WS
+    assert g(A, A, 128, 256, 512, A, A, A, A, MIS, ws, None) == ALIGN
+    assert g(A, A, 0, 256, 512, A, A, A, A, None, 0, None) == OK
+
+
+def test_moe_validation():
+    L = nv.lib()
+    p = nv.MoeProblem(64, 8, 2, 256, 128, 0)
+    t = nv.MoeTensors(*([A] * 9 + [None, None, A]))
+    ws = L.nvfp4_moe_workspace_size(ctypes.byref(p))
+    assert ws > 0
+    run = lambda pp, tt, w, n: L.nvfp4_moe_grouped_gemm(ctypes.byref(pp), ctypes.byref(tt), w, n, None)
+    assert run(p, t, None, 0) == WS
+    assert run(p, t, A, ws - 1) == WS
+    assert run(nv.MoeProblem(64, 8, 2, 250, 128, 0), t, A, ws) == SHAPE
+    assert run(nv.MoeProblem(64, 8, 2, 256, 128, 2), t, A, ws) == SHAPE
+    assert run(nv.MoeProblem(64, 8, 2, 272, 128, 0), t, A, 1 << 40) == UNSUP   # H % 64 != 0
+    assert run(nv.MoeProblem(64, 8, 2, 256, 128, 1), t, A, 1 << 40) == NULL    # W4A4 needs a13/a2
+    t_mis = nv.MoeTensors(*([A] * 8 + [MIS, None, None, A]))
+    assert run(p, t_mis, A, ws) == ALIGN
+    assert run(nv.MoeProblem(0, 8, 2, 256, 128, 0), t, None, 0) == OK
+    assert run(nv.MoeProblem(0, 8, 2, 256, 128, 1), nv.MoeTensors(), None, 0) == OK

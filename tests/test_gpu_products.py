@@ -1,0 +1,158 @@
+"""GPU parity of the GEMV (W4A16), the W4A4 GEMM and the MoE layer against the
+oracle, elementwise |y - ref| <= 1e-3 + 1e-2 |ref|.  Both sides quantize the
+weights themselves (asserted bit-identical) and use their own copy."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_bit_block_amd as nv
+import workloads as wl
+from tests.gpu_common import assert_close, dev, dev_bf16, device, host_bf16_f32, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_both(orc, wb):
+    c0, s0, g0 = orc.quantize(wb)
+    c, s, g = nv.quantize(dev_bf16(wb))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u8(c), c0)
+    np.testing.assert_array_equal(host_u8(s), s0)
+    assert np.float32(g.cpu().item()) == g0
+    return (c0, s0, g0), (c, s, g)
+
+
+@functools.lru_cache(maxsize=None)
+def _layer(name):
+    import oracle
+    w, x = wl.gemv_inputs(name)
+    cpu, gpu = _quant_both(oracle, w)
+    return w, x, cpu, gpu
+
+
+# -------------------------------------------------------------------- GEMV --
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+def test_gemv_tiny(orc, M):
+    w, x = wl.tiny_end_to_end()
+    x = np.concatenate([x, wl.activations(4, 512, seed=77)])[:M]
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    y = nv.gemv_w4a16(dev_bf16(x), c, s, g)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), orc.gemv_w4a16(x, c0, s0, g0), f"gemv M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(200, 2080), (1, 32), (67, 4096)])
+def test_gemv_ragged(orc, N, K):
+    w = wl.layer_weight((N, K), seed=N)
+    x = wl.activations(2, K, seed=K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    y = nv.gemv_w4a16(dev_bf16(x), c, s, g)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), orc.gemv_w4a16(x, c0, s0, g0), f"gemv {N}x{K}")
+
+
+@pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_gemv_layers_sampled(orc, name, M):
+    w, x, (c0, s0, g0), (c, s, g) = _layer(name)
+    xm = x[:M]
+    y = host_bf16_f32(nv.gemv_w4a16(dev_bf16(xm), c, s, g))
+    rows = np.sort(np.random.default_rng(M).choice(w.shape[0], 192, replace=False))
+    ref = orc.gemv_w4a16(xm, c0[rows], s0[rows], g0)
+    assert_close(y[:, rows], ref, f"gemv {name} M={M}")
+
+
+# -------------------------------------------------------------------- GEMM --
+
+def _gemm_case(orc, M, N, K, seed):
+    w = wl.layer_weight((N, K), seed=seed)
+    x = wl.activations(M, K, seed=seed + 1)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))
+    y = nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), orc.gemm_w4a4(x, isc, c0, s0, g0), f"gemm {M}x{N}x{K}")
+
+
+def test_gemm_tiny_end_to_end(orc):
+    w, x = wl.tiny_end_to_end()
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))          # amax(X) / (6 * 448)
+    y = nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), orc.gemm_w4a4(x, isc, c0, s0, g0), "gemm tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (8, 256, 512), (9, 200, 256), (37, 200, 256),
+                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640)])
+def test_gemm_shapes(orc, M, N, K):
+    _gemm_case(orc, M, N, K, seed=M * 7 + N)
+
+
+@pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
+@pytest.mark.parametrize("M", list(wl.GEMM_M_SWEEP))
+def test_gemm_layers_sampled(orc, name, M):
+    w, _, (c0, s0, g0), (c, s, g) = _layer(name)
+    x = wl.activations(M, w.shape[1], seed=4)
+    isc = np.float32(orc.global_scale(x))
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    rng = np.random.default_rng(M)
+    rows = np.sort(rng.choice(M, min(M, 48), replace=False))
+    cols = np.sort(rng.choice(w.shape[0], 96, replace=False))
+    ref = orc.gemm_w4a4(x[rows], isc, c0[cols], s0[cols], g0)
+    assert_close(y[np.ix_(rows, cols)], ref, f"gemm {name} M={M}")
+
+
+def test_gemm_generous_and_tight_input_scale(orc):
+    w = wl.layer_weight((256, 1024), seed=5)
+    x = wl.activations(160, 1024, seed=6)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    for f in (4.0, 0.5):
+        isc = np.float32(orc.global_scale(x) * f)
+        y = nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g)
+        torch.cuda.synchronize()
+        assert_close(host_bf16_f32(y), orc.gemm_w4a4(x, isc, c0, s0, g0), f"gemm scale x{f}")
+
+
+# --------------------------------------------------------------------- MoE --
+
+def _moe_case(orc, T, E, k, H, I, seed):
+    x = wl.activations(T, H, seed=seed)
+    ids, wts = wl.moe_routing(T, E, k, seed=seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    cpu13, cpu2, gpu13, gpu2 = [], [], [], []
+    for e in range(E):
+        a, b = _quant_both(orc, wl.normal_bf16(rng, (2 * I, H), 0.02))
+        cpu13.append(a); gpu13.append(b)
+        a, b = _quant_both(orc, wl.normal_bf16(rng, (H, I), 0.02))
+        cpu2.append(a); gpu2.append(b)
+    cw = [np.stack([q[i] for q in cpu13]) for i in range(2)] + [np.array([q[2] for q in cpu13], np.float32)]
+    cw += [np.stack([q[i] for q in cpu2]) for i in range(2)] + [np.array([q[2] for q in cpu2], np.float32)]
+    gw = [torch.stack([q[i] for q in gpu13]) for i in range(2)] + [torch.cat([q[2] for q in gpu13])]
+    gw += [torch.stack([q[i] for q in gpu2]) for i in range(2)] + [torch.cat([q[2] for q in gpu2])]
+    return x, ids, wts, cw, gw
+
+
+@pytest.mark.parametrize("T,E,k,H,I", [(64, 8, 2, 256, 128), (100, 16, 4, 512, 192), (3, 4, 4, 128, 64)])
+def test_moe_w4a16(orc, T, E, k, H, I):
+    x, ids, wts, cw, gw = _moe_case(orc, T, E, k, H, I, seed=T + E)
+    ref = orc.moe(x, ids, wts, *cw, mode=0)
+    y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A16)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), ref, f"moe w4a16 T={T}")
+
+
+@pytest.mark.parametrize("T,E,k,H,I", [(64, 8, 2, 256, 128), (100, 16, 4, 512, 192)])
+def test_moe_w4a4(orc, T, E, k, H, I):
+    x, ids, wts, cw, gw = _moe_case(orc, T, E, k, H, I, seed=T + E + 1)
+    _, h = orc.moe(x, ids, wts, *cw, mode=0, want_h=True)
+    a13 = (orc.global_scale(x) * (1 + np.arange(E) / 16)).astype(np.float32)
+    a2 = (orc.global_scale(h) * (1 + np.arange(E) / 8)).astype(np.float32)
+    ref = orc.moe(x, ids, wts, *cw, mode=1, a13=a13, a2=a2)
+    y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A4,
+                            a13_scale=dev(a13), a2_scale=dev(a2))
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), ref, f"moe w4a4 T={T}")
