@@ -1,0 +1,345 @@
+"""Throughput of the NVFP4 hot path on one MI355X.
+
+One step = one pass over every kernel of the path on its full-size synthetic
+workload: dynamic quantize and dequantize of a 65536 x 6144 heavy-tailed bf16
+tensor; the W4A16 GEMV at batch 1, 2, 4, 8 on o_proj (6144 x 16384) and
+q_b_proj (16384 x 2048); the W4A4 GEMM at M in {1, 8, ..., 4096} on both
+shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
+6144, intermediate 2048) in W4A16 and W4A4 mode.  Inputs are resident in HBM
+before timing starts.  Weight-streaming kernels cycle through enough weight
+copies that every launch reads its weights from HBM, not from the 256 MB
+last-level cache.
+
+The headline value is the batch-1 o_proj GEMV's effective HBM bandwidth
+(packed codes + scale bytes per launch / mean launch time).  Per-kernel times
+come from HIP events on the stream the kernels run on, around back-to-back
+launches that the host enqueued ahead of the GPU.
+
+Prints one JSON line.  --gpus N with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA
+FP4_PEAK_TFLOPS = 10066.0      # dense MXFP4 (context only)
+METRIC = "NVFP4 bs1 GEMV HBM TB/s; W4A4 GEMM/MoE TFLOPS; % of roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--rows", default="all", help="comma list of row groups: quant,gemv,gemm,moe or all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+class Row:
+    """One kernel configuration: `calls` are zero-argument launchers that
+    enqueue one launch each; `reps` launches per step cycle through them."""
+
+    def __init__(self, name, calls, reps, nbytes=0.0, flops=0.0, info=None, keep=()):
+        self.name, self.calls, self.reps = name, calls, reps
+        self.keep = list(keep)      # device tensors the raw-pointer launches use
+        self.nbytes, self.flops, self.info = nbytes, flops, dict(info or {})
+        self.total_ms = 0.0
+        self.launches = 0
+        self.k = 0
+
+    def enqueue(self):
+        for _ in range(self.reps):
+            self.calls[self.k % len(self.calls)]()
+            self.k += 1
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs the NVFP4 path on exactly one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: there is no multi-GPU path in this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_bit_block_amd as nv
+    import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = nv.lib()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    groups = set(args.rows.split(",")) if args.rows != "all" else {"quant", "gemv", "gemm", "moe"}
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {L.nvfp4_last_error().decode()}")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    t_setup = time.time()
+    rows: list[Row] = []
+
+    def progress(msg):
+        print(f"[bench {time.time() - t_setup:6.1f}s] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ quantize --
+    if "quant" in groups:
+        R, C = 65536, 6144
+        xq = to_dev(wl.heavy_tailed(R, C, seed=1))
+        qc = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+        qs = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
+        qg = torch.empty(4, dtype=torch.float32, device=dev)
+        qws = nv.workspace(nv.quantize_workspace_size(R, C), dev)
+        yq = torch.empty((R, C), dtype=torch.int16, device=dev)
+        qargs = (P(xq), R, C, None, P(qc), P(qs), P(qg), P(qws), qws.numel(), sptr)
+        dargs = (P(qc), P(qs), P(qg), R, C, P(yq), sptr)
+        n = R * C
+        qkeep = (xq, qc, qs, qg, qws, yq)
+        rows.append(Row("quantize_65536x6144", [lambda: check(L.nvfp4_quantize(*qargs), "quantize")], 3, keep=qkeep,
+                        nbytes=n * (2 + 2 + 0.5 + 0.0625),
+                        info={"unique_bytes": n * 2.5625, "bound": "hbm",
+                              "bytes_model": "two-pass: 2 B read (amax) + 2 B read + 0.5625 B written per element"}))
+        progress("quantize workload ready")
+        rows.append(Row("dequantize_65536x6144", [lambda: check(L.nvfp4_dequantize(*dargs), "dequantize")], 3, keep=qkeep,
+                        nbytes=n * (0.5625 + 2), info={"bound": "hbm"}))
+
+    # ---------------------------------------------------------------- GEMV --
+    layers = {}
+    if "gemv" in groups or "gemm" in groups:
+        for name, copies in (("o_proj", 10), ("q_b_proj", 30)):
+            w, x = wl.gemv_inputs(name)
+            N, K = w.shape
+            c, s, g = nv.quantize(to_dev(w))
+            torch.cuda.synchronize()
+            cs = [(c.clone(), s.clone(), g.clone()) for _ in range(copies)]
+            layers[name] = (N, K, cs, to_dev(x))
+            del w
+            progress(f"{name} weights ready ({copies} copies)")
+    if "gemv" in groups:
+        for name, (N, K, cs, x8) in layers.items():
+            for M in wl.GEMV_M:
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                xm = x8[:M].contiguous()
+                calls = []
+                for c, s, g in cs:
+                    a = (P(xm), M, N, K, P(c), P(s), P(g), P(y), sptr)
+                    calls.append(lambda a=a: check(L.nvfp4_gemv_w4a16(*a), "gemv"))
+                wbytes = N * K // 2 + N * K // 16
+                rows.append(Row(f"gemv_w4a16_{name}_M{M}", calls, 2 * len(calls), nbytes=wbytes, keep=(y, xm, cs),
+                                flops=2.0 * M * N * K,
+                                info={"bound": "hbm", "bytes_with_x_y": wbytes + 2 * M * K + 2 * M * N,
+                                      "weight_copies": len(cs)}))
+
+    # ---------------------------------------------------------------- GEMM --
+    if "gemm" in groups:
+        for name, (N, K, cs, _) in layers.items():
+            for M in wl.GEMM_M_SWEEP:
+                x = to_dev(wl.activations(M, K, seed=4))
+                isc = torch.empty(4, dtype=torch.float32, device=dev)
+                # static input_scale = amax(X)/(6*448), taken from the library's dynamic quantize
+                nv.quantize(x, global_scale=isc[:1])
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                ws = nv.workspace(nv.gemm_w4a4_workspace_size(M, N, K), dev)
+                use = cs if M <= 256 else cs[:2]
+                calls = []
+                for c, s, g in use:
+                    a = (P(x), P(isc), M, N, K, P(c), P(s), P(g), P(y), P(ws), ws.numel(), sptr)
+                    calls.append(lambda a=a: check(L.nvfp4_gemm_w4a4(*a), "gemm"))
+                reps = max(2, min(2 * len(calls), (4 * 4096) // max(M, 1)))
+                wbytes = N * K // 2 + N * K // 16
+                rows.append(Row(f"gemm_w4a4_{name}_M{M}", calls, reps, nbytes=wbytes + 2 * M * K + 2 * M * N,
+                                keep=(x, isc, y, ws, use),
+                                flops=2.0 * M * N * K, info={"M": M, "N": N, "K": K}))
+
+    # ----------------------------------------------------------------- MoE --
+    if "moe" in groups:
+        T, E, k, H, I = wl.MOE_T, wl.MOE_E, wl.MOE_TOPK, wl.MOE_H, wl.MOE_I
+        ids, wts = wl.moe_routing(T, E, k, seed=5)
+        xm = to_dev(wl.moe_tokens(T, H, seed=55))
+        w13c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+        w13s = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
+        w13g = torch.empty(E, dtype=torch.float32, device=dev)
+        w2c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+        w2s = torch.empty((E, H, I // 16), dtype=torch.uint8, device=dev)
+        w2g = torch.empty(E, dtype=torch.float32, device=dev)
+        for e, w13, w2 in wl.moe_expert_weights_iter(E, H, I, seed=50, threads=16):
+            nv.quantize(to_dev(w13), codes=w13c[e], scales=w13s[e], global_scale=w13g[e:e + 1])
+            nv.quantize(to_dev(w2), codes=w2c[e], scales=w2s[e], global_scale=w2g[e:e + 1])
+            if e % 32 == 31:
+                progress(f"moe experts {e + 1}/{E} quantized")
+        ids_d = torch.from_numpy(ids).to(dev)
+        wts_d = torch.from_numpy(wts).to(dev)
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
+        # static input scales, one per expert: a13 = amax(X)/(6*448) from the
+        # library's dynamic quantize of X; a2 is a generous analytic estimate
+        # for h = silu(g)*u with g, u ~ N(0, s2), s2 = H * 0.02^2 * E[x^2]:
+        # |h| stays below s2 * ln(#h) with margin, doubled (the pages' static
+        # input_scale is likewise a generous per-tensor heuristic).
+        a13 = torch.empty(E, dtype=torch.float32, device=dev)
+        tmp = torch.empty(4, dtype=torch.float32, device=dev)
+        nv.quantize(xm, global_scale=tmp[:1])
+        a13[:] = tmp[0]
+        s2 = H * 0.02 ** 2
+        a2 = torch.full((E,), 2.0 * s2 * float(np.log(T * k * I)) / 2688.0, dtype=torch.float32, device=dev)
+        moe_bytes = E * (2 * I * H + H * I) * (0.5 + 1 / 16) + 2 * T * H * 2
+        moe_flops = 2.0 * T * k * (2 * I * H + H * I)
+        for mode in (0, 1):
+            p = nv.MoeProblem(T, E, k, H, I, mode)
+            ws = nv.workspace(L.nvfp4_moe_workspace_size(ctypes.byref(p)), dev)
+            tens = nv.MoeTensors(xm.data_ptr(), ids_d.data_ptr(), wts_d.data_ptr(), w13c.data_ptr(),
+                                 w13s.data_ptr(), w13g.data_ptr(), w2c.data_ptr(), w2s.data_ptr(),
+                                 w2g.data_ptr(), a13.data_ptr() if mode else None,
+                                 a2.data_ptr() if mode else None, out.data_ptr())
+            a = (ctypes.byref(p), ctypes.byref(tens), P(ws), ws.numel(), sptr)
+            call = (lambda a=a, p=p, tens=tens, ws=ws: check(L.nvfp4_moe_grouped_gemm(*a), "moe"))
+            rows.append(Row(f"moe_{'w4a16' if mode == 0 else 'w4a4'}", [call], 1, nbytes=moe_bytes,
+                            keep=(xm, ids_d, wts_d, w13c, w13s, w13g, w2c, w2s, w2g, a13, a2, out, ws),
+                            flops=moe_flops, info={"T": T, "E": E, "top_k": k, "H": H, "I": I,
+                                                   "bytes_model": "NVFP4 expert weights + x + out"}))
+
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    # ------------------------------------------------------------- timing --
+    sleeper = _Sleeper(torch)
+
+    def step(record):
+        for r in rows:
+            sleeper.prefill(r)
+            if record:
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+            r.enqueue()
+            if record:
+                ev1.record(stream)
+                r._ev = (ev0, ev1)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    progress(f"warmup done; timing {args.steps} steps")
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        events.append([(r, r._ev) for r in rows])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for per_step in events:
+        for r, (e0, e1) in per_step:
+            r.total_ms += e0.elapsed_time(e1)
+            r.launches += r.reps
+
+    report = {}
+    for r in rows:
+        us = 1e3 * r.total_ms / max(r.launches, 1)
+        d = {"us_per_launch": round(us, 3)}
+        if r.nbytes:
+            gbs = r.nbytes / (us * 1e-6) / 1e9
+            d["GB_s"] = round(gbs, 1)
+            d["frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+        if r.flops:
+            tf = r.flops / (us * 1e-6) / 1e12
+            d["TFLOPS"] = round(tf, 2)
+            d["frac_mfma_f16_peak"] = round(tf / MFMA_F16_PEAK_TFLOPS, 4)
+        d.update({k: v for k, v in r.info.items() if k not in ("M", "N", "K")})
+        report[r.name] = d
+
+    head = report.get("gemv_w4a16_o_proj_M1")
+    value = head["GB_s"] / 1e3 if head else None
+    roofline = None
+    if head:
+        roofline = {"kernel": "k_gemv<1> (nvfp4_gemv_w4a16, o_proj 6144x16384, M=1)", "bound": "hbm",
+                    "achieved": head["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(head["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "bytes_per_launch": 6144 * 16384 // 2 + 6144 * 16384 // 16,
+                    "us_per_launch": head["us_per_launch"]}
+    progress("timed steps done")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": None if value is None else round(value, 4), "unit": "TB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * (t1 - t0) / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws, bf16; NVFP4 weights quantized on the GPU)",
+        "config": {"workload": "W4A16 batch-1 decode GEMV on NVFP4 o_proj [6144 x 16384]; step also runs "
+                               "quantize/dequantize 65536x6144, GEMV M=1..8 on o_proj and q_b_proj, "
+                               "W4A4 GEMM M=1..4096 on both, MoE T=4096 E=256 top-8 H=6144 I=2048",
+                   "gpu": torch.cuda.get_device_name(0), "setup_s": round(setup_s, 1),
+                   "timing": "HIP events around back-to-back launches enqueued behind a prefill kernel"},
+        "roofline": roofline, "cpu_baseline": cpu, "rows": report,
+    }
+    print(json.dumps(line))
+
+
+class _Sleeper:
+    """Enqueues a short GPU spin before each row so the host can queue that
+    row's launches ahead of the GPU (the events then time GPU work only)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ok = hasattr(torch.cuda, "_sleep")
+        self.cycles = 2_000_000
+        if self.ok:
+            try:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.cuda._sleep(self.cycles)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                self.cycles = int(self.cycles * min(4.0, max(0.05, 1.0 / max(ms, 1e-3))))  # ~1 ms
+            except Exception:
+                self.ok = False
+
+    def prefill(self, row):
+        if self.ok:
+            self.torch.cuda._sleep(self.cycles)
+
+
+def cpu_baseline(target_s: float):
+    """The oracle (as it stands) on the host cores: W4A16 GEMV over the full
+    o_proj weight at batch 1, repeated until about `target_s` seconds."""
+    import oracle
+    import workloads as wl
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    w, x = wl.gemv_inputs("o_proj")
+    c, s, g = oracle.quantize(w)
+    x1 = x[:1]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv_w4a16(x1, c, s, g)
+        n += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    wbytes = c.nbytes + s.nbytes
+    return {"value": round(wbytes / dt / 1e12, 6), "unit": "TB/s", "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
+            "kind": "oracle", "sample": f"W4A16 GEMV o_proj 6144x16384 at M=1 (fp64 oracle incl. its dequantize), "
+                                        f"{n} calls, {dt:.3f} s per call"}
+
+
+if __name__ == "__main__":
+    main()

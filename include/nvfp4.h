@@ -22,7 +22,10 @@
  * Conventions for every entry point:
  *   - Tensors are device pointers to contiguous row-major storage; bf16 is
  *     passed as uint16_t bit patterns, codes and scale bytes as uint8_t.
- *     Every tensor base pointer must be 16-byte aligned (ALIGN otherwise).
+ *     Tensor base pointers (bf16, codes, scale bytes, outputs, workspace) must
+ *     be 16-byte aligned; fp32 scale pointers and the MoE routing arrays
+ *     (int32 ids, fp32 weights, per-expert fp32 scales) 4-byte aligned
+ *     (ALIGN otherwise).
  *   - Scalars that live with the tensors (global scales, input_scale) are
  *     device pointers to fp32, so no call reads device memory on the host.
  *   - The caller allocates and frees every buffer, workspace included; the

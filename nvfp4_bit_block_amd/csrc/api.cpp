@@ -26,6 +26,7 @@ int32_t hip_status(hipError_t e, const char* where) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -146,8 +147,8 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const floa
     if (rows == 0) return NVFP4_OK;
     if (!x || !codes || !scales || !global_scale)
         return fail(NVFP4_ERR_NULL_ARG, "quantize: x, codes, scales and global_scale are required%s");
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(global_scale) ||
-        (static_scale && !aligned16(static_scale)) || (workspace && !aligned16(workspace)))
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(global_scale) ||
+        (static_scale && !aligned4(static_scale)) || (workspace && !aligned16(workspace)))
         return fail(NVFP4_ERR_ALIGN, "quantize: pointers must be 16-byte aligned%s");
     const size_t need = static_scale ? 0 : nvfp4_quantize_workspace_size(rows, cols);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -183,7 +184,7 @@ int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const floa
     if (rows == 0) return NVFP4_OK;
     if (!codes || !scales || !global_scale || !y)
         return fail(NVFP4_ERR_NULL_ARG, "dequantize: all pointers are required%s");
-    if (!aligned16(codes) || !aligned16(scales) || !aligned16(global_scale) || !aligned16(y))
+    if (!aligned16(codes) || !aligned16(scales) || !aligned4(global_scale) || !aligned16(y))
         return fail(NVFP4_ERR_ALIGN, "dequantize: pointers must be 16-byte aligned%s");
     return hip_status(launch_dequantize(codes, scales, global_scale, 0.0f, rows, cols, y, as_stream(stream)),
                       "dequantize");
@@ -201,7 +202,7 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!x || !w_codes || !w_scales || !w_global || !y)
         return fail(NVFP4_ERR_NULL_ARG, "gemv: all pointers are required%s");
-    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_global) || !aligned16(y))
+    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned4(w_global) || !aligned16(y))
         return fail(NVFP4_ERR_ALIGN, "gemv: pointers must be 16-byte aligned%s");
     return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y,
                                         as_stream(stream)),
@@ -225,8 +226,8 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!x || !input_scale || !w_codes || !w_scales || !w_global || !y)
         return fail(NVFP4_ERR_NULL_ARG, "gemm: x, input_scale, weights and y are required%s");
-    if (!aligned16(x) || !aligned16(input_scale) || !aligned16(w_codes) || !aligned16(w_scales) ||
-        !aligned16(w_global) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    if (!aligned16(x) || !aligned4(input_scale) || !aligned16(w_codes) || !aligned16(w_scales) ||
+        !aligned4(w_global) || !aligned16(y) || (workspace && !aligned16(workspace)))
         return fail(NVFP4_ERR_ALIGN, "gemm: pointers must be 16-byte aligned%s");
     const GemmLayout l = layout_gemm(M, N, K);
     if (!workspace || workspace_bytes < l.total)
@@ -302,12 +303,14 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         !t->w2_codes || !t->w2_scales || !t->w2_global || !t->out ||
         (p->mode == 1 && (!t->a13_scale || !t->a2_scale)))
         return fail(NVFP4_ERR_NULL_ARG, "moe: a required tensor is NULL%s");
-    const void* ptrs[] = {t->x, t->topk_ids, t->topk_weights, t->w13_codes, t->w13_scales, t->w13_global,
-                          t->w2_codes, t->w2_scales, t->w2_global, t->out};
-    for (const void* q : ptrs)
-        if (!aligned16(q)) return fail(NVFP4_ERR_ALIGN, "moe: pointers must be 16-byte aligned%s");
-    if (p->mode == 1 && (!aligned16(t->a13_scale) || !aligned16(t->a2_scale)))
-        return fail(NVFP4_ERR_ALIGN, "moe: pointers must be 16-byte aligned%s");
+    const void* tensors[] = {t->x, t->w13_codes, t->w13_scales, t->w2_codes, t->w2_scales, t->out};
+    for (const void* q : tensors)
+        if (!aligned16(q)) return fail(NVFP4_ERR_ALIGN, "moe: tensor pointers must be 16-byte aligned%s");
+    const void* words[] = {t->topk_ids, t->topk_weights, t->w13_global, t->w2_global};
+    for (const void* q : words)
+        if (!aligned4(q)) return fail(NVFP4_ERR_ALIGN, "moe: fp32/int32 arrays must be 4-byte aligned%s");
+    if (p->mode == 1 && (!aligned4(t->a13_scale) || !aligned4(t->a2_scale)))
+        return fail(NVFP4_ERR_ALIGN, "moe: fp32/int32 arrays must be 4-byte aligned%s");
     if (workspace && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "moe: workspace must be 16-byte aligned%s");
     const MoeLayout l = layout_moe(*p);
     if (!workspace || workspace_bytes < l.total)

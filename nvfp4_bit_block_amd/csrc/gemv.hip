@@ -4,14 +4,25 @@
 // model card targets ("What this variant changes": batch-1 decode GEMVs are
 // pure weight bandwidth): y[m, n] = Sg * sum_b s[n, b] * sum_{k in b} q[n, k] x[m, k].
 //
-// One wavefront owns one output row at a time.  Each lane streams 16-byte
-// chunks of packed codes (32 elements = two 16-element blocks) with the two
-// matching scale bytes, decodes the codes to exact bf16 grid values with the
-// gfx950 FP4 -> bf16 conversion, forms per-block partial dot products with
-// v_dot2_f32_bf16 (fp32 accumulation), applies the block scale once per
-// block, and the row sum is reduced across the wave at the end.
+// The kernel is HBM-bound: it must keep enough weight bytes in flight and
+// spend only ~1-2 VALU lane-ops per weight element.  Layout of the work:
+//   * a wavefront owns RW output rows at a time; lane l owns the 32-element
+//     chunks c = l + 64 j (j < NCH) of each row, so every 16-byte load
+//     instruction of the wave reads 1 KB of contiguous packed codes;
+//   * all NCH chunk loads (and their 2 scale bytes) of the RW rows are issued
+//     before any is used, so a wave has RW*NCH KB in flight;
+//   * codes are decoded to exact bf16 grid values by the gfx950 FP4 -> bf16
+//     conversion (one instruction per two elements) and multiplied with the
+//     activation by v_dot2_f32_bf16, one fp32 partial per 16-element block,
+//     scaled once per block;
+//   * the activation is read once per workgroup: kept in VGPRs when a lane's
+//     slice is small (NCH * M <= 2 chunks), else staged in LDS;
+//   * row sums are reduced across the wave with cross-lane shuffles.
+// Weights are read with non-temporal loads: each byte is used once.
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
+
+#include <type_traits>
 
 namespace nvfp4 {
 
@@ -20,82 +31,319 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float dot2(bf16x2 a, uint32_t b_bits, float c) {
-    bf16x2 b = __builtin_bit_cast(bf16x2, b_bits);
-    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b_bits), c, false);
 }
 
-template <int M>
+// Partial dot products of one 32-element chunk (two blocks) with M activation
+// rows; x4(m, i) returns the i-th 16-byte piece (8 bf16) of row m's chunk.
+template <int M, typename XF>
+__device__ __forceinline__ void chunk_dot(uint4 q, uint32_t s2, XF x4, float acc[M]) {
+    const f32x2 sc = e4m3x2_to_f32(s2);
+    const float s0 = sc.x, s1 = sc.y;
+    bf16x2 wv[16];
+    fp4x8_to_bf16(q.x, &wv[0]);
+    fp4x8_to_bf16(q.y, &wv[4]);
+    fp4x8_to_bf16(q.z, &wv[8]);
+    fp4x8_to_bf16(q.w, &wv[12]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint4 xa = x4(m, 0), xb = x4(m, 1), xc = x4(m, 2), xd = x4(m, 3);
+        float p0 = 0.0f, p1 = 0.0f;
+        p0 = dot2(wv[0], xa.x, p0);
+        p0 = dot2(wv[1], xa.y, p0);
+        p0 = dot2(wv[2], xa.z, p0);
+        p0 = dot2(wv[3], xa.w, p0);
+        p0 = dot2(wv[4], xb.x, p0);
+        p0 = dot2(wv[5], xb.y, p0);
+        p0 = dot2(wv[6], xb.z, p0);
+        p0 = dot2(wv[7], xb.w, p0);
+        p1 = dot2(wv[8], xc.x, p1);
+        p1 = dot2(wv[9], xc.y, p1);
+        p1 = dot2(wv[10], xc.z, p1);
+        p1 = dot2(wv[11], xc.w, p1);
+        p1 = dot2(wv[12], xd.x, p1);
+        p1 = dot2(wv[13], xd.y, p1);
+        p1 = dot2(wv[14], xd.z, p1);
+        p1 = dot2(wv[15], xd.w, p1);
+        acc[m] = __builtin_fmaf(s0, p0, acc[m]);
+        acc[m] = __builtin_fmaf(s1, p1, acc[m]);
+    }
+}
+
+// Activation in LDS, transposed so that lanes reading the same 16-byte piece
+// of consecutive chunks hit consecutive LDS addresses (no bank conflicts):
+// piece p (8 bf16) of chunk c of row m lives at [(m * 4 + p) * nchunk + c].
+template <int M, int THREADS>
+__device__ __forceinline__ void stage_x_lds(uint4* xlds, const uint16_t* __restrict__ x, int64_t K) {
+    const uint4* src = reinterpret_cast<const uint4*>(x);
+    const int64_t per_row = K / 8, nchunk = K / 32;
+    for (int64_t g = threadIdx.x; g < (int64_t)M * per_row; g += THREADS) {
+        const int64_t m = g / per_row, r = g - m * per_row;
+        xlds[(m * 4 + (r & 3)) * nchunk + (r >> 2)] = src[g];
+    }
+    __syncthreads();
+}
+
+// Weight fragment: for RW rows, NCH 16-byte code chunks and their two scale
+// bytes per lane.
+template <int RW, int NCH>
+struct Frag {
+    uint4 q[RW][NCH];
+    uint32_t s[RW][NCH];
+};
+
+// Fixed chunk layout: K == KS * NCH * 2048.  A workgroup of 4 waves forms
+// 4/KS row groups of KS waves; the KS waves of a group split K (wave part p
+// owns chunks p*64*NCH + lane + 64*j, j < NCH), so each lane keeps only its
+// NCH chunks of the activation in VGPRs.  A row group walks its batches of RW
+// rows with one fragment of registers: the registers of chunk j are refilled
+// with the next batch's chunk j right after use, so a whole fragment of loads
+// is in flight while the wave computes.  The last batch is peeled so the
+// refill is unconditional (no register copies).  Partial row sums are reduced
+// across the wave with shuffles and, when KS > 1, across the group's waves
+// through LDS.
+template <int M, int NCH, int KS, int RW, bool CONTIG = false>
 __global__ __launch_bounds__(kThreads) void k_gemv(const uint16_t* __restrict__ x, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ wc,
                                                    const uint8_t* __restrict__ ws,
                                                    const float* __restrict__ g0,
                                                    const float* __restrict__ g1,
                                                    uint16_t* __restrict__ y) {
+    constexpr int kWavesPerBlock = kThreads / kWave;
+    constexpr int kGroups = kWavesPerBlock / KS;
+    static_assert(kWavesPerBlock % KS == 0, "row groups");
+    __shared__ float red[2][kWavesPerBlock][RW][M];
+
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int grp = wave / KS, part = wave % KS;
+    const int64_t KB = K / 2, KS16 = K / 16;
+    // chunk of (lane, j): interleaved (lane + 64 j: every load instruction of
+    // the wave reads 1 KB contiguous) or, with CONTIG, lane-contiguous
+    // (NCH * lane + j: a lane's scale bytes are adjacent and come in one load)
+    const int64_t cbase = (int64_t)part * 64 * NCH;
+    auto chunk = [&](int j) -> int64_t { return CONTIG ? cbase + NCH * lane + j : cbase + lane + 64 * j; };
+
+    // batches of RW rows: this group owns b = gid, gid + ngroups, ...
+    const int64_t nbatch = (N + RW - 1) / RW;
+    const int64_t gid = (int64_t)blockIdx.x * kGroups + grp;
+    const int64_t ngroups = (int64_t)gridDim.x * kGroups;
+    // every wave of a workgroup runs the same number of iterations (the LDS
+    // reduction synchronizes them); batches past the end are computed on a
+    // clamped row and not stored
+    const int64_t iters = (nbatch + ngroups - 1) / ngroups;
+    const int64_t blk_first = (int64_t)blockIdx.x * kGroups;
+    const int64_t my_iters = (KS > 1) ? iters : (gid < nbatch ? (nbatch - 1 - gid) / ngroups + 1 : 0);
+    (void)blk_first;
+
+    // one row's chunks and scale pairs into fragment slot r
+    auto load_row = [&](Frag<RW, NCH>& f, int r, const uint8_t* wrow, const uint16_t* srow) {
+        if constexpr (CONTIG) {
+            static_assert(NCH == 2 || NCH == 4, "contiguous scale load");
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) f.q[r][j] = *reinterpret_cast<const uint4*>(wrow + chunk(j) * 16);
+            if constexpr (NCH == 2) {
+                const uint32_t sw = *reinterpret_cast<const uint32_t*>(srow + chunk(0));
+                f.s[r][0] = sw & 0xFFFFu;
+                f.s[r][1] = sw >> 16;
+            } else {
+                const uint2 sw = *reinterpret_cast<const uint2*>(srow + chunk(0));
+                f.s[r][0] = sw.x & 0xFFFFu; f.s[r][1] = sw.x >> 16;
+                f.s[r][2] = sw.y & 0xFFFFu; f.s[r][3] = sw.y >> 16;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                f.q[r][j] = load_nt16(wrow + chunk(j) * 16);
+                f.s[r][j] = __builtin_nontemporal_load(srow + chunk(j));
+            }
+        }
+    };
+
+    auto load = [&](Frag<RW, NCH>& f, int64_t b) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const int64_t row = min(b * RW + r, N - 1);
+            const uint8_t* wrow = wc + row * KB;
+            const uint16_t* srow = reinterpret_cast<const uint16_t*>(ws + row * KS16);
+            load_row(f, r, wrow, srow);
+        }
+    };
+
+    Frag<RW, NCH> f;
+    if (my_iters > 0) load(f, gid);
+
+    uint4 xr[M * NCH * 4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint4* p = reinterpret_cast<const uint4*>(x + m * K + chunk(j) * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[(m * NCH + j) * 4 + i] = p[i];
+        }
+    const float scale = *g0 * (g1 ? *g1 : 1.0f);
+
+    auto finish = [&](float (&acc)[RW][M], int64_t b, int it) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = wave_sum_lane63(acc[r][m]);
+        if constexpr (KS == 1) {
+            if (lane == kWave - 1 && b < nbatch) {
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    if (b * RW + r >= N) break;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        y[m * N + b * RW + r] = (uint16_t)f32_to_bf16_rne(acc[r][m] * scale);
+                }
+            }
+        } else {
+            const int buf = it & 1;
+            if (lane == kWave - 1) {
+#pragma unroll
+                for (int r = 0; r < RW; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) red[buf][wave][r][m] = acc[r][m];
+            }
+            __syncthreads();
+            if (part == 0 && lane < RW * M && b < nbatch) {
+                const int r = lane / M, m = lane % M;
+                float v = 0.0f;
+#pragma unroll
+                for (int p = 0; p < KS; ++p) v += red[buf][grp * KS + p][r][m];
+                if (b * RW + r < N) y[m * N + b * RW + r] = (uint16_t)f32_to_bf16_rne(v * scale);
+            }
+        }
+    };
+
+    // compute the batch held in f; with PREFETCH, refill f with batch bn
+    auto compute = [&](auto prefetch, float (&acc)[RW][M], int64_t bn) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const int64_t row = min(bn * RW + r, N - 1);
+            const uint8_t* wrow = wc + row * KB;
+            const uint16_t* srow = reinterpret_cast<const uint16_t*>(ws + row * KS16);
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                chunk_dot<M>(f.q[r][j], f.s[r][j],
+                             [&](int m, int i) { return xr[(m * NCH + j) * 4 + i]; }, acc[r]);
+            if constexpr (decltype(prefetch)::value) load_row(f, r, wrow, srow);
+        }
+    };
+
+    int64_t b = gid;
+    for (int64_t it = 0; it + 1 < my_iters; ++it, b += ngroups) {
+        float acc[RW][M] = {};
+        compute(std::true_type{}, acc, b + ngroups);
+        finish(acc, b, (int)it);
+    }
+    if (my_iters > 0) {
+        float acc[RW][M] = {};
+        compute(std::false_type{}, acc, 0);
+        finish(acc, b, (int)(my_iters - 1));
+    }
+}
+
+// Any K % 32 == 0: chunk loop at run time, four chunks in flight per lane;
+// activation from LDS when it fits, else from global memory.
+template <int M, bool XLDS, int THREADS>
+__global__ __launch_bounds__(THREADS) void k_gemv_any(const uint16_t* __restrict__ x, int64_t N,
+                                                      int64_t K, const uint8_t* __restrict__ wc,
+                                                      const uint8_t* __restrict__ ws,
+                                                      const float* __restrict__ g0,
+                                                      const float* __restrict__ g1,
+                                                      uint16_t* __restrict__ y) {
+    extern __shared__ uint4 xlds[];
+    constexpr int kWavesPerBlock = THREADS / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
     const float scale = *g0 * (g1 ? *g1 : 1.0f);
     const int64_t nchunk = K / 32;
-    for (int64_t n = (int64_t)blockIdx.x * (kThreads / kWave) + (threadIdx.x / kWave); n < N;
-         n += nwaves) {
+    const int64_t KB = K / 2, KS = K / 16;
+    if constexpr (XLDS) stage_x_lds<M, THREADS>(xlds, x, K);
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave); n < N; n += nwaves) {
         float acc[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-        const uint4* wrow = reinterpret_cast<const uint4*>(wc + n * (K / 2));
-        const uint16_t* srow = reinterpret_cast<const uint16_t*>(ws + n * (K / 16));
-#pragma unroll 2
-        for (int64_t c = lane; c < nchunk; c += kWave) {
-            const uint4 q = load_nt16(&wrow[c]);
-            const uint32_t s2 = __builtin_nontemporal_load(&srow[c]);
-            const float s0 = e4m3_to_f32(s2 & 0xFFu);
-            const float s1 = e4m3_to_f32(s2 >> 8);
-            bf16x2 wv[16];
-            fp4x8_to_bf16(q.x, &wv[0]);
-            fp4x8_to_bf16(q.y, &wv[4]);
-            fp4x8_to_bf16(q.z, &wv[8]);
-            fp4x8_to_bf16(q.w, &wv[12]);
+        const uint8_t* wrow = wc + n * KB;
+        const uint16_t* srow = reinterpret_cast<const uint16_t*>(ws + n * KS);
+        for (int64_t c0 = lane; c0 < nchunk; c0 += 4 * kWave) {
+            uint4 q[4];
+            uint32_t s[4];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const uint4* xr = reinterpret_cast<const uint4*>(x + m * K + c * 32);
-                const uint4 xa = xr[0], xb = xr[1], xc = xr[2], xd = xr[3];
-                float p0 = 0.0f, p1 = 0.0f;
-                p0 = dot2(wv[0], xa.x, p0);
-                p0 = dot2(wv[1], xa.y, p0);
-                p0 = dot2(wv[2], xa.z, p0);
-                p0 = dot2(wv[3], xa.w, p0);
-                p0 = dot2(wv[4], xb.x, p0);
-                p0 = dot2(wv[5], xb.y, p0);
-                p0 = dot2(wv[6], xb.z, p0);
-                p0 = dot2(wv[7], xb.w, p0);
-                p1 = dot2(wv[8], xc.x, p1);
-                p1 = dot2(wv[9], xc.y, p1);
-                p1 = dot2(wv[10], xc.z, p1);
-                p1 = dot2(wv[11], xc.w, p1);
-                p1 = dot2(wv[12], xd.x, p1);
-                p1 = dot2(wv[13], xd.y, p1);
-                p1 = dot2(wv[14], xd.z, p1);
-                p1 = dot2(wv[15], xd.w, p1);
-                acc[m] = __builtin_fmaf(s0, p0, acc[m]);
-                acc[m] = __builtin_fmaf(s1, p1, acc[m]);
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = min(c0 + u * kWave, nchunk - 1);
+                q[u] = load_nt16(wrow + c * 16);
+                s[u] = __builtin_nontemporal_load(srow + c);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = c0 + u * kWave;
+                if (c < nchunk) {
+                    chunk_dot<M>(q[u], s[u],
+                                 [&](int m, int i) {
+                                     if constexpr (XLDS) return xlds[(m * 4 + i) * nchunk + c];
+                                     else return reinterpret_cast<const uint4*>(x + m * K + c * 32)[i];
+                                 },
+                                 acc);
+                }
             }
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = wave_sum(acc[m]);
-        if (lane == 0) {
+        for (int m = 0; m < M; ++m) acc[m] = wave_sum_lane63(acc[m]);
+        if (lane == kWave - 1) {
 #pragma unroll
             for (int m = 0; m < M; ++m) y[m * N + n] = (uint16_t)f32_to_bf16_rne(acc[m] * scale);
         }
     }
 }
 
+constexpr int64_t kMaxLdsBytes = 64 * 1024;
+
+// Grid: about `blocks_per_cu` workgroups per CU on a 256-CU chip, never
+// more than there are row batches.
+template <int M, int NCH, int KS, int RW, bool CONTIG = false>
+hipError_t launch_cfg(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
+                      const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
+                      int blocks_per_cu) {
+    constexpr int64_t groups = (kThreads / kWave) / KS;
+    const int64_t nbatch = (N + RW - 1) / RW;
+    int64_t grid = min((int64_t)256 * blocks_per_cu, (nbatch + groups - 1) / groups);
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, CONTIG>), dim3((unsigned)grid), dim3(kThreads), 0, stream, x, N, K,
+                       wc, ws, g0, g1, y);
+    return hipGetLastError();
+}
+
+template <int M, bool XLDS>
+hipError_t launch_any(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
+                      const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
+    int64_t grid = (N + 3) / 4;
+    if (grid > 2048) grid = 2048;
+    const size_t lds = XLDS ? (size_t)M * (size_t)K * 2 : 0;
+    hipLaunchKernelGGL((k_gemv_any<M, XLDS, kThreads>), dim3((unsigned)grid), dim3(kThreads), lds, stream,
+                       x, N, K, wc, ws, g0, g1, y);
+    return hipGetLastError();
+}
+
 template <int M>
 hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                     const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
-    const int64_t waves_per_block = kThreads / kWave;
-    int64_t grid = (N + waves_per_block - 1) / waves_per_block;
-    if (grid > 65535) grid = 65535;
-    hipLaunchKernelGGL(k_gemv<M>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, N, K, wc, ws,
-                       g0, g1, y);
-    return hipGetLastError();
+    const bool fits_lds = (int64_t)M * K * 2 <= kMaxLdsBytes;
+    // measured on MI355X: one wave per 2048-wide row with four rows in
+    // flight for K = 2048; four waves splitting K with two rows in flight for
+    // K = 16384 (two workgroups per CU in both cases)
+    if (K == 2048) {
+        if constexpr (M <= 4) return launch_cfg<M, 1, 1, 4>(x, N, K, wc, ws, g0, g1, y, stream, 3);
+        else return launch_cfg<M, 1, 1, 2>(x, N, K, wc, ws, g0, g1, y, stream, 3);
+    }
+    if (K == 16384) {
+        if constexpr (M <= 4) return launch_cfg<M, 2, 4, 2>(x, N, K, wc, ws, g0, g1, y, stream, 2);
+    }
+    if (fits_lds) return launch_any<M, true>(x, N, K, wc, ws, g0, g1, y, stream);
+    return launch_any<M, false>(x, N, K, wc, ws, g0, g1, y, stream);
 }
 
 }  // namespace

@@ -115,6 +115,31 @@ __device__ __forceinline__ uint4 fp4x8_scaled_bf16_bits(uint32_t w, float s) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Two E4M3 scale bytes (bits 0-7 and 8-15 of w) -> fp32 pair, exact, with
+// the gfx950 FP8 (E4M3) -> f32 conversion.
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+}
+
+// DPP lane shuffle of a float (lanes masked off by ROW_MASK read 0).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wave with six DPP adds; the total lands in
+// lane 63 (other lanes hold partial sums).
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v += dpp_f32<0xB1>(v);         // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);         // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);        // row_half_mirror: 8-lane sums
+    v += dpp_f32<0x140>(v);        // row_mirror: 16-lane sums
+    v += dpp_f32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -1,5 +1,8 @@
 """The C-ABI library loads, exports every declared entry point, and rejects
-invalid arguments on the host (no GPU needed: checks run before any HIP call)."""
+invalid arguments on the host (no GPU needed: checks run before any HIP call).
+
+Every call below either fails a host-side check or is a zero-size no-op, so no
+kernel is ever launched with the fake addresses used here."""
 import ctypes
 import os
 
@@ -61,6 +64,7 @@ def test_gemv_validation():
     assert g(A, 9, 8, 64, A, A, A, A, None) == UNSUP
     assert g(A, 1, 8, 48, A, A, A, A, None) == UNSUP                 # K % 32 != 0
     assert g(A, 1, 8, 64, A, A, MIS, A, None) == ALIGN
+    assert g(A, 1, 8, 64, A, A, A, A + 2, None) == ALIGN
     assert g(A, 0, 8, 64, A, A, A, A, None) == OK
     assert g(A, 3, 0, 64, A, A, A, A, None) == OK
 
@@ -94,5 +98,7 @@ def test_moe_validation():
     assert run(nv.MoeProblem(64, 8, 2, 256, 128, 1), t, A, 1 << 40) == NULL    # W4A4 needs a13/a2
     t_mis = nv.MoeTensors(*([A] * 8 + [MIS, None, None, A]))
     assert run(p, t_mis, A, ws) == ALIGN
+    t_words = nv.MoeTensors(*([A, A + 4, A + 8, A, A, A + 12, A, A, A + 4, None, None, A]))
+    assert run(p, t_words, A, ws - 1) == WS     # 4-byte aligned fp32/int32 arrays pass the alignment check
     assert run(nv.MoeProblem(0, 8, 2, 256, 128, 0), t, None, 0) == OK
     assert run(nv.MoeProblem(0, 8, 2, 256, 128, 1), nv.MoeTensors(), None, 0) == OK
