@@ -86,8 +86,68 @@ def saturation(static_scale: float = 1e-3):
     return to_bf16_bits(x), static_scale
 
 
+def _tie_block(d, bmax, rng):
+    """A block holding bmax and the E2M1 midpoints of divisor d (both signs,
+    with bf16 neighbours where d is not a power of two)."""
+    vals = [bmax]
+    for m in _E2M1_MIDS:
+        vals.append(m * d)
+        vals.append(-m * d)
+    while len(vals) < 16:
+        vals.append(float(rng.uniform(-1.0, 1.0)) * bmax)
+    return np.array(vals[:16], np.float64)
+
+
+def extreme_global_scales():
+    """Static global scales that put block divisors d = s * Sg at the edges of
+    the range where a quantizer may divide through a reciprocal, on both sides
+    of it: Sg = 2^-103 gives d = 2^-100 exactly for a block whose scale is 8
+    and d just below it for scale 7.5; Sg = 2^-120 gives divisors near 2^-114
+    and, with subnormal bf16 elements, subnormal fp32 divisors; Sg = 2^124
+    gives d above and below 2^125."""
+    rng = np.random.default_rng(77)
+    out = {}
+    sg = 2.0 ** -103
+    t = 6.0 * sg
+    blocks = [_tie_block(8.0 * sg, 8.0 * t, rng), _tie_block(7.5 * sg, 7.5 * t, rng),
+              _tie_block(2.0 ** -100, 6.0 * 2.0 ** -100, rng)]
+    out["edge_2m100"] = (to_bf16_bits(np.concatenate(blocks).astype(np.float32)).reshape(1, -1), sg)
+    sg = 2.0 ** -120
+    blk = _tie_block(44.0 * sg, 2.0 ** -112, rng)
+    sub = np.zeros(16)
+    sub[0] = 2.0 ** -126
+    sub[1] = -(2.0 ** -130)
+    sub[2] = 2.0 ** -133
+    sub[3] = -(2.0 ** -127)
+    out["tiny_global"] = (to_bf16_bits(np.concatenate([blk, sub]).astype(np.float32)).reshape(1, -1), sg)
+    sg = 2.0 ** 124
+    big = np.full(16, 0.0)
+    big[:8] = [3.0e38, -2.0e38, 1.0e38, -5.0e37, 2.5e38, 1.5e38, -3.2e38, 7.0e37]
+    mid = _tie_block(0.6875 * sg, 2.0 ** 126, rng)
+    out["huge_global"] = (to_bf16_bits(np.concatenate([big, mid]).astype(np.float32)).reshape(1, -1), sg)
+    return out
+
+
+def subnormal_scale_ratio():
+    """Dynamic mode, amax 448 (Sg = fl(1/6), t = 1): a block whose maximum
+    1.4453125 * 2^-9 rounds to the smallest E4M3 scale 2^-9, so its elements
+    reach about 8.7 times the divisor (saturated codes), next to ordinary
+    blocks."""
+    rng = np.random.default_rng(78)
+    amax_blk = rng.standard_normal(16) * 50.0
+    amax_blk[5] = 448.0
+    b = 1.4453125 * 2.0 ** -9
+    odd = rng.uniform(-1.0, 1.0, 16) * b
+    odd[0] = b
+    odd[1] = -b
+    odd[2] = b * 0.93
+    return to_bf16_bits(np.concatenate([amax_blk, odd]).astype(np.float32)).reshape(1, -1), None
+
+
 def all_cases():
     return {
+        **extreme_global_scales(),
+        "subnormal_scale_ratio": subnormal_scale_ratio(),
         "e2m1_ties": e2m1_ties(),
         "e4m3_ties": e4m3_ties(),
         "scale_edges": scale_edge_cases(),
