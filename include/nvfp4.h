@@ -122,9 +122,11 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
  * X bf16 [M, K] is quantized to NVFP4 under the device fp32 *input_scale
  * (same arithmetic as nvfp4_quantize in static mode), then
  * y[m, n] = bf16( input_scale * Sg_w * sum_b sx[m,b] sw[n,b] sum_{k in b} qx qw ),
- * fp32 accumulation.  w_* as in the GEMV; y bf16 [M, N].  K % 64 == 0 (else
- * UNSUPPORTED).  Workspace: nvfp4_gemm_w4a4_workspace_size(M, N, K) bytes
- * (the quantized X and, for small M, split-K partial sums).
+ * fp32 accumulation.  w_* as in the GEMV; y bf16 [M, N].  K % 64 == 0, and
+ * for M > 8 the weight codes must span less than 2 GiB (N * K / 2 < 2^31);
+ * else UNSUPPORTED.  Workspace: nvfp4_gemm_w4a4_workspace_size(M, N, K)
+ * bytes (the quantized X, held as its exact products q * s in 16-bit form,
+ * and, for small M, split-K partial sums).
  * ------------------------------------------------------------------------ */
 size_t nvfp4_gemm_w4a4_workspace_size(int64_t M, int64_t N, int64_t K);
 int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, int64_t N, int64_t K,

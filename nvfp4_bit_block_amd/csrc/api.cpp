@@ -33,43 +33,53 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // ----------------------------------------------------------- GEMM planning --
 
 struct GemmPlan {
-    bool gemv = false;   // M <= 8: dequantized activation + GEMV
-    Tile tile = Tile::k128x128;
-    int bm = 128;
+    bool gemv = false;   // M <= 8: decoded activation + GEMV
+    A16Tile tile = A16Tile::k256x256_w128x64;
     int ksplit = 1;
-    int64_t grid_m = 0;
 };
 
+// Tile and split-K choice for the W4A4 GEMM (measured on MI355X: the
+// 256x256 tile with eight 128x64 waves is the fastest per tile; smaller tiles
+// win where 256x256 leaves most CUs idle; small M streams the weights once
+// and splits K to spread that stream over the chip).
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
     if (M <= 8) {
         p.gemv = true;
         return p;
     }
-    if (M > 64) { p.tile = Tile::k128x128; p.bm = 128; }
-    else if (M > 32) { p.tile = Tile::k64x128; p.bm = 64; }
-    else { p.tile = Tile::k32x128; p.bm = 32; }
-    p.grid_m = (M + p.bm - 1) / p.bm;
-    const int64_t tiles = p.grid_m * ((N + 127) / 128);
-    const int64_t kchunks = K / 64;
-    while (tiles * p.ksplit < 512 && p.ksplit < 16 && kchunks / (p.ksplit * 2) >= 4) p.ksplit *= 2;
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    if (M <= 32) p.tile = A16Tile::k32x256_w32x64;
+    else if (M <= 64) p.tile = A16Tile::k64x256_w64x64;
+    else if (M <= 128 || big < 192) p.tile = A16Tile::k128x128_w64x64;
+    else p.tile = A16Tile::k256x256_w128x64;
+    const int64_t bm = a16_tile_rows(p.tile), bn = a16_tile_cols(p.tile);
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int64_t ksteps = K / 64;
+    while (tiles * p.ksplit < 256 && p.ksplit < 16 && ksteps / (p.ksplit * 2) >= 8) p.ksplit *= 2;
     return p;
 }
 
+// Rows of the activation handled per GEMM launch: the kernel addresses the
+// decoded activation through one buffer resource, which spans < 2 GiB.
+int64_t gemm_chunk_rows(int64_t M, int64_t K) {
+    int64_t cap = (kRdMaxBytes - 1) / (K * 2);
+    if (cap >= 256) cap = cap / 256 * 256;
+    return cap < M ? cap : M;
+}
+
 struct GemmLayout {
-    size_t xq_codes = 0, xq_scales = 0, xhat = 0, partial = 0, total = 0;
+    size_t xhat = 0, partial = 0, total = 0;
 };
 
 GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
     GemmLayout l;
     const GemmPlan p = plan_gemm(M, N, K);
     size_t off = 0;
-    l.xq_codes = off; off += align_up((size_t)(M * K / 2));
-    l.xq_scales = off; off += align_up((size_t)(M * K / 16));
-    if (p.gemv) {
-        l.xhat = off; off += align_up((size_t)(M * K * 2));
-    } else if (p.ksplit > 1) {
-        l.partial = off; off += align_up((size_t)p.ksplit * (size_t)(M * N) * 4);
+    l.xhat = off; off += align_up((size_t)(M * K * 2));
+    if (!p.gemv && p.ksplit > 1) {
+        const int64_t rows = gemm_chunk_rows(M, K);
+        l.partial = off; off += align_up((size_t)p.ksplit * (size_t)(rows * N) * 4);
     }
     l.total = off;
     return l;
@@ -223,6 +233,8 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
         return fail(NVFP4_ERR_SHAPE, "gemm: need M, N >= 0, K > 0 and K %% 16 == 0%s");
     if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm: K must be a multiple of 64%s");
+    if (M > 8 && ((int64_t)N * (K / 2) >= kRdMaxBytes || gemm_chunk_rows(M, K) < 1))
+        return fail(NVFP4_ERR_UNSUPPORTED, "gemm: weight matrix of 2 GiB or more%s");
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!x || !input_scale || !w_codes || !w_scales || !w_global || !y)
         return fail(NVFP4_ERR_NULL_ARG, "gemm: x, input_scale, weights and y are required%s");
@@ -234,51 +246,54 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
         return fail(NVFP4_ERR_WORKSPACE, "gemm: workspace smaller than nvfp4_gemm_w4a4_workspace_size%s");
     hipStream_t s = as_stream(stream);
     const GemmPlan p = plan_gemm(M, N, K);
-    uint8_t* xc = at<uint8_t>(workspace, l.xq_codes);
-    uint8_t* xs = at<uint8_t>(workspace, l.xq_scales);
-    // static activation quantization under input_scale
+    // Static activation quantization under input_scale.  The GEMM consumes the
+    // quantized activation as the exact products q * s (f16 for the MFMA path,
+    // bf16 for the GEMV), written directly by the quantizer; the two global
+    // scales are applied after the contraction.
+    uint16_t* xh = at<uint16_t>(workspace, l.xhat);
     PackArgs a;
     a.x = x;
     a.rows = M;
     a.cols = K;
     a.mode = ScaleMode::kStatic;
     a.sg_ptr = input_scale;
-    a.codes = xc;
-    a.scales = xs;
+    a.xhat = xh;
+    a.xhat_bf16 = p.gemv;
     int32_t st = hip_status(launch_quantize_pack(a, s), "gemm activation quantize");
     if (st) return st;
-    if (p.gemv) {
-        // q * s of the activation is exact in bf16; the product of the two
-        // global scales is applied by the GEMV.
-        uint16_t* xh = at<uint16_t>(workspace, l.xhat);
-        st = hip_status(launch_dequantize(xc, xs, nullptr, 1.0f, M, K, xh, s), "gemm activation decode");
-        if (st) return st;
+    if (p.gemv)
         return hip_status(launch_gemv_w4a16(xh, (int)M, N, K, w_codes, w_scales, w_global, input_scale, y, s),
                           "gemm gemv");
-    }
-    GemmArgs g;
-    g.a = xc;
-    g.a_scales = xs;
-    g.a_global = input_scale;
-    g.b_codes = w_codes;
-    g.b_scales = w_scales;
-    g.b_global = w_global;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.ksplit = p.ksplit;
-    if (p.ksplit > 1) {
-        float* part = at<float>(workspace, l.partial);
-        g.out = part;
-        g.ldo = N;
-        st = hip_status(launch_gemm(g, AFmt::kFp4, Epi::kPartialF32, p.tile, (int)p.grid_m, s), "gemm");
+    const int64_t chunk = gemm_chunk_rows(M, K);
+    for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+        const int64_t rows = (M - r0 < chunk) ? M - r0 : chunk;
+        GemmArgs g;
+        g.a = xh + r0 * K;
+        g.a_src_rows = rows;
+        g.a_global = input_scale;
+        g.b_codes = w_codes;
+        g.b_scales = w_scales;
+        g.b_global = w_global;
+        g.M = rows;
+        g.N = N;
+        g.K = K;
+        g.ksplit = p.ksplit;
+        if (p.ksplit > 1) {
+            float* part = at<float>(workspace, l.partial);
+            g.out = part;
+            g.ldo = N;
+            st = hip_status(launch_gemm_a16(g, AFmt::kF16, Epi::kPartialF32, p.tile, 0, s), "gemm");
+            if (st) return st;
+            st = hip_status(launch_splitk_reduce(part, p.ksplit, rows, N, input_scale, w_global, y + r0 * N, s),
+                            "gemm split-k reduce");
+        } else {
+            g.out = y + r0 * N;
+            g.ldo = N;
+            st = hip_status(launch_gemm_a16(g, AFmt::kF16, Epi::kStoreBf16, p.tile, 0, s), "gemm");
+        }
         if (st) return st;
-        return hip_status(launch_splitk_reduce(part, p.ksplit, M, N, input_scale, w_global, y, s),
-                          "gemm split-k reduce");
     }
-    g.out = y;
-    g.ldo = N;
-    return hip_status(launch_gemm(g, AFmt::kFp4, Epi::kStoreBf16, p.tile, (int)p.grid_m, s), "gemm");
+    return NVFP4_OK;
 }
 
 // --------------------------------------------------------------------- MoE --

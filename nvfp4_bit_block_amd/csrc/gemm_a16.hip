@@ -1,0 +1,436 @@
+// gemm_a16.hip -- NVFP4-weight GEMM with a 16-bit activation operand:
+// Y = A * W^T, A [M, K] f16 (the exact values q * s of an NVFP4-quantized
+// activation: the W4A4 path) or bf16 (the W4A16 path), W NVFP4 [N, K].
+//
+// Fprop with the contraction axis innermost on both operands ("Getting
+// GLM-5.2 NVFP4 Post-Training off the ground", "Going deeper" and "TN, NT,
+// and what actually binds"); W4A4 and W4A16 per the model card
+// "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "Kernel choice".
+//
+// Scale application: weight elements are decoded to q * s, exact in f16 and
+// in bf16, and multiplied on v_mfma_f32_32x32x16_{f16,bf16} with fp32
+// accumulation; the global scales are applied in the epilogue.  gfx950's
+// scaled MFMA takes one power-of-two scale per 32 elements and its fp4
+// conversions use only the exponent of their scale operand, so neither can
+// carry a per-16 E4M3 scale; decoding costs VALU work, which is why the
+// activation arrives already decoded (its quantizer writes q * s directly)
+// and only the weight tile is decoded here, once per wave that uses it.
+//
+// Data movement, per 64-wide K step (double-buffered in LDS, one barrier per
+// step): the workgroup loads the A tile (BM rows x 128 bytes, 8 lanes per
+// row) and the packed B tile (BN rows x 32 code bytes + 4 scale bytes)
+// through registers into LDS.  Waves read A fragments and packed B fragments
+// from LDS, decode B in registers and issue the MFMAs.
+//
+// K order inside a step: the 32x32x16 MFMA takes, in lane l, row (or column)
+// l % 32 and 8 consecutive K positions selected by l / 32.  A K permutation
+// applied to both operands leaves the product unchanged, so lane half
+// hf = l / 32 takes K positions [32 hf, 32 hf + 32) of the step and MFMA kk
+// uses positions 32 hf + 8 kk + [0, 8): a lane's packed B share is 16
+// contiguous code bytes and two scale bytes.
+//
+// LDS rows are padded (A: 144 bytes, B codes: 48 bytes) so that the 16-byte
+// reads of 16 consecutive rows fall on distinct banks.
+#include "nvfp4_device.hpp"
+#include "nvfp4_internal.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer built here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes < 0x80000000ull ? (uint32_t)bytes : 0x80000000u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload4(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <AFmt AF>
+struct OpOf;
+template <>
+struct OpOf<AFmt::kF16> {
+    using T = f16x8;
+};
+template <>
+struct OpOf<AFmt::kBf16> {
+    using T = bf16x8;
+};
+
+// Eight weight codes (one word) -> eight operand values q * s (exact).
+__device__ __forceinline__ f16x8 decode_w(uint32_t w, float s, f16x8*) {
+    return fp4x8_scaled_f16(w, (_Float16)s);
+}
+__device__ __forceinline__ bf16x8 decode_w(uint32_t w, float s, bf16x8*) {
+    return __builtin_bit_cast(bf16x8, fp4x8_scaled_bf16_bits(w, s));
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int kk) {
+    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
+}
+
+constexpr int kRowA = 144;   // LDS bytes per A row per step (128 + 16 of padding)
+constexpr int kRowB = 48;    // LDS bytes per B row of codes per step (32 + 16 of padding)
+constexpr int kGroupM = 8;   // m-tiles per band in the ungrouped tile order
+
+template <int TM, int TN, int WM, int WN>
+struct Cfg {
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int WTM = 32 * TM, WTN = 32 * TN;
+    static constexpr int BM = WTM * WM, BN = WTN * WN;
+    static constexpr int A_BYTES = BM * kRowA, BC_BYTES = BN * kRowB, BS_BYTES = BN * 4;
+    static constexpr int STAGE = A_BYTES + BC_BYTES + BS_BYTES;
+    // per-thread share of one step's copy
+    static constexpr int A_CHUNKS = BM * 8;                // 16-byte chunks of A
+    static constexpr int A_PER_T = A_CHUNKS / NT;
+    static constexpr int B_CHUNKS = BN * 2;                // 16-byte chunks of B codes
+    static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
+    static_assert(A_CHUNKS % NT == 0, "A copy");
+    static_assert(BN <= NT, "one scale word per thread");
+    static_assert(2 * STAGE <= 160 * 1024, "LDS");
+};
+
+template <int TM, int TN, int WM, int WN, AFmt AF, Epi EP>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
+    using C = Cfg<TM, TN, WM, WN>;
+    using Op = typename OpOf<AF>::T;
+    constexpr int BM = C::BM, BN = C::BN, WTM = C::WTM, WTN = C::WTN;
+    static_assert(EP != Epi::kMoeGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
+    __shared__ __align__(16) uint8_t smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int c32 = lane & 31, hf = lane >> 5;
+
+    // ---- tile, group and K range of this workgroup
+    int grp = 0, tn, kz;
+    int64_t row_beg, row_end;
+    if (g.groups > 0) {
+        const int mt = (int)blockIdx.y;
+        if (mt >= g.tile_off[g.groups]) return;
+        int lo = 0, hi = g.groups;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (g.tile_off[mid] <= mt) lo = mid; else hi = mid;
+        }
+        grp = lo;
+        row_beg = (int64_t)g.row_off[grp] + (int64_t)(mt - g.tile_off[grp]) * BM;
+        row_end = min((int64_t)g.row_off[grp + 1], row_beg + BM);
+        tn = (int)blockIdx.x;
+        kz = (int)blockIdx.z;
+    } else {
+        // Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber
+        // so that each XCD receives a contiguous run of tiles, and walk tiles in
+        // bands of kGroupM m-tiles so that concurrently running tiles share rows
+        // of A and columns of B in that XCD's L2.
+        const int nwg = (int)gridDim.x;
+        int id = (int)blockIdx.x;
+        if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+        const int mtiles = (int)((g.M + BM - 1) / BM);
+        const int ntiles = (int)((g.N + BN - 1) / BN);
+        const int per_split = mtiles * ntiles;
+        kz = id / per_split;
+        const int t = id - kz * per_split;
+        const int band = t / (kGroupM * ntiles);
+        const int first_m = band * kGroupM;
+        const int gsz = min(mtiles - first_m, kGroupM);
+        const int r = t - band * kGroupM * ntiles;
+        const int tm = first_m + r % gsz;
+        tn = r / gsz;
+        row_beg = (int64_t)tm * BM;
+        row_end = min(g.M, row_beg + BM);
+    }
+    const int ksteps = (int)(g.K / 64);
+    const int per = (ksteps + g.ksplit - 1) / g.ksplit;
+    const int kc0 = __builtin_amdgcn_readfirstlane(kz * per);
+    const int nsteps = __builtin_amdgcn_readfirstlane(max(0, min(ksteps - kc0, per)));
+
+    const uint32_t KB = (uint32_t)(g.K / 2), KS = (uint32_t)(g.K / 16), KA = (uint32_t)(g.K * 2);
+    // A: 16-bit rows, optionally gathered, one resource over the source tensor
+    // (the host keeps it below 2 GiB)
+    const Rsrc ra = make_rsrc(g.a, (uint64_t)g.a_src_rows * KA);
+    const Rsrc rb_c = make_rsrc(g.b_codes + (int64_t)grp * g.N * KB, (uint64_t)g.N * KB);
+    const Rsrc rb_s = make_rsrc(g.b_scales + (int64_t)grp * g.N * KS, (uint64_t)g.N * KS);
+
+    // ---- this thread's copy assignments (fixed for the whole K loop)
+    // A: chunk p = tid + NT * u -> row p / 8, 16-byte chunk p % 8 of the row's step
+    uint32_t va[C::A_PER_T], la[C::A_PER_T];
+#pragma unroll
+    for (int u = 0; u < C::A_PER_T; ++u) {
+        const int p = tid + C::NT * u, r = p >> 3, cc = p & 7;
+        const int64_t row = row_beg + r;
+        uint32_t v = kOob;
+        if (row < row_end) {
+            const int64_t src = g.a_rows ? (int64_t)(g.a_rows[row] / g.a_div) : row;
+            v = (uint32_t)(src * KA) + 16u * cc;
+        }
+        va[u] = v;
+        la[u] = r * kRowA + 16 * cc;
+    }
+    // Global column of tile column n (or -1 past the end).
+    auto b_col = [&](int n) -> int64_t {
+        if constexpr (EP == Epi::kMoeGateUp) {
+            // column block j of wave w: gate columns for j < TN/2, the matching
+            // up columns (I further) for j >= TN/2
+            const int w = n / WTN, j = (n % WTN) / 32, cc = n % 32;
+            const int jj = j % (TN / 2 > 0 ? TN / 2 : 1);
+            const int64_t hcol = (int64_t)tn * (BN / 2) + w * (WTN / 2) + 32 * jj + cc;
+            if (hcol >= g.half_n) return -1;
+            return (j < TN / 2) ? hcol : g.half_n + hcol;
+        } else {
+            const int64_t col = (int64_t)tn * BN + n;
+            return col < g.N ? col : -1;
+        }
+    };
+    // B codes: chunk p = tid + NT * u (p < 2 BN) -> column p / 2, half p % 2
+    uint32_t vbc[C::B_PER_T], lbc[C::B_PER_T];
+#pragma unroll
+    for (int u = 0; u < C::B_PER_T; ++u) {
+        const int p = tid + C::NT * u;
+        const int n = p >> 1, h2 = p & 1;
+        uint32_t v = kOob;
+        if (p < C::B_CHUNKS) {
+            const int64_t col = b_col(n);
+            if (col >= 0) v = (uint32_t)col * KB + 16u * h2;
+        }
+        vbc[u] = v;
+        lbc[u] = C::A_BYTES + (p < C::B_CHUNKS ? n * kRowB + 16 * h2 : 0);
+    }
+    // B scales: thread tid < BN copies column tid's 4 scale bytes of the step
+    uint32_t vbs = kOob;
+    if (tid < BN) {
+        const int64_t col = b_col(tid);
+        if (col >= 0) vbs = (uint32_t)col * KS;
+    }
+    const uint32_t lbs = C::A_BYTES + C::BC_BYTES + 4 * (tid < BN ? tid : 0);
+
+    uint4 ra_st[C::A_PER_T], rb_st[C::B_PER_T];
+    uint32_t rs_st = 0;
+    auto load_step = [&](int kc) {
+#pragma unroll
+        for (int u = 0; u < C::A_PER_T; ++u) ra_st[u] = bload16(ra, va[u], (uint32_t)kc * 128u);
+#pragma unroll
+        for (int u = 0; u < C::B_PER_T; ++u) rb_st[u] = bload16(rb_c, vbc[u], (uint32_t)kc * 32u);
+        rs_st = bload4(rb_s, vbs, (uint32_t)kc * 4u);
+    };
+    auto store_step = [&](int buf) {
+        uint8_t* base = smem + buf * C::STAGE;
+#pragma unroll
+        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la[u]) = ra_st[u];
+#pragma unroll
+        for (int u = 0; u < C::B_PER_T; ++u)
+            if (tid + C::NT * u < C::B_CHUNKS) *reinterpret_cast<uint4*>(base + lbc[u]) = rb_st[u];
+        if (tid < BN) *reinterpret_cast<uint32_t*>(base + lbs) = rs_st;
+    };
+
+    // ---- fragment addresses within a stage buffer
+    uint32_t fa[TM], fbc[TN], fbs[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = (wm * WTM + 32 * i + c32) * kRowA + 64 * hf;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = wn * WTN + 32 * j + c32;
+        fbc[j] = C::A_BYTES + n * kRowB + 16 * hf;
+        fbs[j] = C::A_BYTES + C::BC_BYTES + 4 * n;
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // One K step from LDS buffer `buf`: the A fragments of MFMA group kk + 1
+    // are requested before the MFMAs of group kk are issued (the scheduling
+    // barriers keep that order; left alone, the scheduler re-reads fragments
+    // just in time to save registers and the MFMAs wait on LDS latency).
+    auto compute_step = [&](int buf) {
+        const uint8_t* base = smem + buf * C::STAGE;
+        uint4 cb[TN];
+        f32x2 sb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            cb[j] = *reinterpret_cast<const uint4*>(base + fbc[j]);
+            sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(base + fbs[j]) >> (16 * hf));
+        }
+        Op av[2][TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[0][i] = *reinterpret_cast<const Op*>(base + fa[i]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    av[(kk + 1) & 1][i] = *reinterpret_cast<const Op*>(base + fa[i] + 16 * (kk + 1));
+            }
+            Op bv[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bv[j] = decode_w(word(cb[j], kk), kk < 2 ? sb[j].x : sb[j].y, (Op*)nullptr);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma(av[kk & 1][i], bv[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- main loop, one barrier per step: iteration s multiplies buffer s % 2
+    // while the loads of step s + 1 are in flight, then stores step s + 1 into
+    // the other buffer (last read in iteration s - 1, before the previous
+    // barrier) and starts the loads of step s + 2.
+    if (nsteps > 0) {
+        load_step(kc0);
+        store_step(0);
+        if (nsteps > 1) load_step(kc0 + 1);
+        __syncthreads();
+    }
+    for (int s = 0; s < nsteps; ++s) {
+        compute_step(s & 1);
+        if (s + 1 < nsteps) {
+            store_step((s + 1) & 1);
+            if (s + 2 < nsteps) load_step(kc0 + s + 2);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32
+    const int gi = g.groups > 0 ? grp : 0;
+    const float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = row_beg + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (row >= row_end) continue;
+            if constexpr (EP == Epi::kMoeGateUp) {
+#pragma unroll
+                for (int j = 0; j < TN / 2; ++j) {
+                    const int64_t hcol = (int64_t)tn * (BN / 2) + wn * (WTN / 2) + 32 * j + c32;
+                    if (hcol >= g.half_n) continue;
+                    const float gv = acc[i][j][r] * sc;
+                    const float uv = acc[i][j + TN / 2][r] * sc;
+                    const float hv = gv / (1.0f + expf(-gv)) * uv;
+                    reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + hcol] = (uint16_t)f32_to_bf16_rne(hv);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t col = (int64_t)tn * BN + wn * WTN + 32 * j + c32;
+                    if (col >= g.N) continue;
+                    const float v = acc[i][j][r];
+                    if constexpr (EP == Epi::kStoreBf16) {
+                        reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(v * sc);
+                    } else if constexpr (EP == Epi::kPartialF32) {
+                        reinterpret_cast<float*>(g.out)[((int64_t)kz * g.M + row) * g.ldo + col] = v;
+                    } else {
+                        reinterpret_cast<float*>(g.out)[row * g.ldo + col] = v * sc;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int TM, int TN, int WM, int WN, AFmt AF, Epi EP>
+hipError_t launch_cfg(const GemmArgs& g, int grid_m, hipStream_t stream) {
+    using C = Cfg<TM, TN, WM, WN>;
+    dim3 grid;
+    if (g.groups > 0) {
+        const int64_t ncols = (EP == Epi::kMoeGateUp) ? g.half_n : g.N;
+        const int64_t bn = (EP == Epi::kMoeGateUp) ? C::BN / 2 : C::BN;
+        grid = dim3((unsigned)((ncols + bn - 1) / bn), (unsigned)grid_m, (unsigned)g.ksplit);
+    } else {
+        const int64_t tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
+        grid = dim3((unsigned)tiles);
+    }
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, AF, EP>), grid, dim3(C::NT), 0, stream, g);
+    return hipGetLastError();
+}
+
+template <AFmt AF, Epi EP>
+hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t stream) {
+    switch (tile) {
+        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, AF, EP>(g, grid_m, stream);
+        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, AF, EP>(g, grid_m, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int a16_tile_rows(A16Tile t) {
+    switch (t) {
+        case A16Tile::k256x256_w128x64: return 256;
+        case A16Tile::k256x256_w128x128: return 256;
+        case A16Tile::k256x128_w128x64: return 256;
+        case A16Tile::k256x128_w64x64: return 256;
+        case A16Tile::k128x256_w64x128: return 128;
+        case A16Tile::k128x128_w64x64: return 128;
+        case A16Tile::k128x128_w32x64: return 128;
+        case A16Tile::k64x256_w64x64: return 64;
+        case A16Tile::k32x256_w32x64: return 32;
+    }
+    return 0;
+}
+
+int a16_tile_cols(A16Tile t) {
+    switch (t) {
+        case A16Tile::k256x256_w128x64: return 256;
+        case A16Tile::k256x256_w128x128: return 256;
+        case A16Tile::k256x128_w128x64: return 128;
+        case A16Tile::k256x128_w64x64: return 128;
+        case A16Tile::k128x256_w64x128: return 256;
+        case A16Tile::k128x128_w64x64: return 128;
+        case A16Tile::k128x128_w32x64: return 128;
+        case A16Tile::k64x256_w64x64: return 256;
+        case A16Tile::k32x256_w32x64: return 256;
+    }
+    return 0;
+}
+
+hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, int grid_m,
+                           hipStream_t stream) {
+#define NVFP4_EPI(AF)                                                                     \
+    switch (epi) {                                                                        \
+        case Epi::kStoreBf16: return launch_tile<AF, Epi::kStoreBf16>(g, tile, grid_m, stream);   \
+        case Epi::kPartialF32: return launch_tile<AF, Epi::kPartialF32>(g, tile, grid_m, stream); \
+        case Epi::kMoeGateUp: return launch_tile<AF, Epi::kMoeGateUp>(g, tile, grid_m, stream);   \
+        case Epi::kMoeDown: return launch_tile<AF, Epi::kMoeDown>(g, tile, grid_m, stream);       \
+    }
+    switch (afmt) {
+        case AFmt::kF16: NVFP4_EPI(AFmt::kF16) break;
+        case AFmt::kBf16: NVFP4_EPI(AFmt::kBf16) break;
+        default: break;
+    }
+#undef NVFP4_EPI
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

@@ -184,8 +184,22 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
         uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         uint2 codes;
         uint32_t s8 = encode_block(w, Sg, t, codes);
-        reinterpret_cast<uint2*>(a.codes)[b] = codes;
-        a.scales[b] = (uint8_t)s8;
+        if (a.codes != nullptr) {
+            reinterpret_cast<uint2*>(a.codes)[b] = codes;
+            a.scales[b] = (uint8_t)s8;
+        }
+        if (a.xhat != nullptr) {
+            // q * s for the 16 elements, exact in f16 and bf16
+            const float s = e4m3_to_f32(s8);
+            uint4* dst = reinterpret_cast<uint4*>(a.xhat + r * a.cols + cb * 16);
+            if (a.xhat_bf16) {
+                dst[0] = fp4x8_scaled_bf16_bits(codes.x, s);
+                dst[1] = fp4x8_scaled_bf16_bits(codes.y, s);
+            } else {
+                dst[0] = __builtin_bit_cast(uint4, fp4x8_scaled_f16(codes.x, (_Float16)s));
+                dst[1] = __builtin_bit_cast(uint4, fp4x8_scaled_f16(codes.y, (_Float16)s));
+            }
+        }
     }
 }
 
