@@ -147,8 +147,13 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
  * w13_codes [E, 2I, H/2], w13_scales [E, 2I, H/16], w13_global fp32 [E];
  * w2_codes [E, H, I/2], w2_scales [E, H, I/16], w2_global fp32 [E];
  * a13_scale, a2_scale fp32 [E] (mode 1 only, else may be NULL); out bf16 [T, H].
- * H % 64 == 0 and I % 64 == 0 (else UNSUPPORTED).  Routing, grouping, both
- * grouped GEMMs and the combine run on the device with no host round trip.
+ * H % 64 == 0 and I % 64 == 0, and every operand the grouped GEMMs read
+ * below 2 GiB (T*H*2 for mode 0 or T*top_k*H*2 for mode 1, T*top_k*I*2,
+ * the codes of one expert's W13 and W2); else UNSUPPORTED.  Routing,
+ * grouping, both grouped GEMMs and the combine run on the device with no
+ * host round trip.  Workspace: nvfp4_moe_workspace_size(p) bytes (routing
+ * tables, h, the fp32 per-slot outputs and, for mode 1, the quantized
+ * activations held as their exact products q * s in f16).
  * ------------------------------------------------------------------------ */
 typedef struct nvfp4_moe_problem {
     int64_t T;      /* tokens */

@@ -87,11 +87,15 @@ GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
 
 // ------------------------------------------------------------ MoE planning --
 
+// Row tile of the grouped GEMMs (a group's rows are covered by tiles of this
+// height; measured on MI355X, 128-row tiles at three workgroups per CU beat
+// 160- and 256-row tiles that read each expert's weights only once but run
+// one wave per SIMD).
 constexpr int kMoeBM = 128;
 
 struct MoeLayout {
     size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0;
-    size_t xq_codes = 0, xq_scales = 0, hq_codes = 0, hq_scales = 0, h = 0, y = 0, total = 0;
+    size_t xq = 0, hq = 0, h = 0, y = 0, total = 0;
 };
 
 MoeLayout layout_moe(const nvfp4_moe_problem& p) {
@@ -104,10 +108,9 @@ MoeLayout layout_moe(const nvfp4_moe_problem& p) {
     l.inv = off; off += align_up(S * 4);
     l.pos_group = off; off += align_up(S * 4);
     if (p.mode == 1) {
-        l.xq_codes = off; off += align_up(S * (size_t)p.H / 2);
-        l.xq_scales = off; off += align_up(S * (size_t)p.H / 16);
-        l.hq_codes = off; off += align_up(S * (size_t)p.I / 2);
-        l.hq_scales = off; off += align_up(S * (size_t)p.I / 16);
+        // the quantized activations as exact f16 products q * s, slot order
+        l.xq = off; off += align_up(S * (size_t)p.H * 2);
+        l.hq = off; off += align_up(S * (size_t)p.I * 2);
     }
     l.h = off; off += align_up(S * (size_t)p.I * 2);
     l.y = off; off += align_up(S * (size_t)p.H * 4);
@@ -313,6 +316,14 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     if (p->H % 64 || p->I % 64) return fail(NVFP4_ERR_UNSUPPORTED, "moe: H and I must be multiples of 64%s");
     if (p->E > 4096) return fail(NVFP4_ERR_UNSUPPORTED, "moe: at most 4096 experts%s");
     if (p->T * p->top_k > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "moe: too many slots%s");
+    {
+        // the GEMM kernels address each operand through one buffer resource
+        const int64_t S = p->T * p->top_k;
+        const int64_t act = p->mode == 1 ? S * p->H * 2 : p->T * p->H * 2;
+        if (act >= kRdMaxBytes || S * p->I * 2 >= kRdMaxBytes || 2 * p->I * (p->H / 2) >= kRdMaxBytes ||
+            p->H * (p->I / 2) >= kRdMaxBytes)
+            return fail(NVFP4_ERR_UNSUPPORTED, "moe: an operand of 2 GiB or more%s");
+    }
     if (p->T == 0) return NVFP4_OK;
     if (!t->x || !t->topk_ids || !t->topk_weights || !t->w13_codes || !t->w13_scales || !t->w13_global ||
         !t->w2_codes || !t->w2_scales || !t->w2_global || !t->out ||
@@ -346,7 +357,10 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     if (st) return st;
     const int grid_m = (int)((S + kMoeBM - 1) / kMoeBM + E);
 
-    // GEMM 1: [g | u] = x^ W13^T, h = bf16(silu(g) * u)
+    // GEMM 1: [g | u] = x^ W13^T, h = bf16(silu(g) * u).  W4A16 multiplies the
+    // bf16 tokens (gathered by slot); W4A4 first quantizes them per expert
+    // group under a13_scale into their exact f16 products q * s.
+    const A16Tile tile = A16Tile::k128x128_w64x64;  // kMoeBM-row tiles, as the routing counted
     GemmArgs g1;
     g1.b_codes = t->w13_codes;
     g1.b_scales = t->w13_scales;
@@ -362,8 +376,7 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     g1.half_n = p->I;
     AFmt af = AFmt::kBf16;
     if (p->mode == 1) {
-        uint8_t* xc = at<uint8_t>(workspace, l.xq_codes);
-        uint8_t* xs = at<uint8_t>(workspace, l.xq_scales);
+        uint16_t* xq = at<uint16_t>(workspace, l.xq);
         PackArgs a;
         a.x = t->x;
         a.rows = S;
@@ -374,20 +387,20 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         a.mode = ScaleMode::kGrouped;
         a.sg_group = t->a13_scale;
         a.row_group = pos_group;
-        a.codes = xc;
-        a.scales = xs;
+        a.xhat = xq;
         st = hip_status(launch_quantize_pack(a, s), "moe activation quantize");
         if (st) return st;
-        g1.a = xc;
-        g1.a_scales = xs;
+        g1.a = xq;
+        g1.a_src_rows = S;
         g1.a_global = t->a13_scale;
-        af = AFmt::kFp4;
+        af = AFmt::kF16;
     } else {
         g1.a = t->x;
         g1.a_rows = perm;
         g1.a_div = (int32_t)p->top_k;
+        g1.a_src_rows = p->T;
     }
-    st = hip_status(launch_gemm(g1, af, Epi::kMoeGateUp, Tile::k128x128, grid_m, s), "moe gemm1");
+    st = hip_status(launch_gemm_a16(g1, af, Epi::kMoeGateUp, tile, grid_m, s), "moe gemm1");
     if (st) return st;
 
     // GEMM 2: Y = h^ W2^T (fp32, per slot row)
@@ -403,9 +416,9 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     g2.groups = E;
     g2.out = Y;
     g2.ldo = p->H;
+    g2.a_src_rows = S;
     if (p->mode == 1) {
-        uint8_t* hc = at<uint8_t>(workspace, l.hq_codes);
-        uint8_t* hs = at<uint8_t>(workspace, l.hq_scales);
+        uint16_t* hq = at<uint16_t>(workspace, l.hq);
         PackArgs a;
         a.x = h;
         a.rows = S;
@@ -414,17 +427,15 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         a.mode = ScaleMode::kGrouped;
         a.sg_group = t->a2_scale;
         a.row_group = pos_group;
-        a.codes = hc;
-        a.scales = hs;
+        a.xhat = hq;
         st = hip_status(launch_quantize_pack(a, s), "moe intermediate quantize");
         if (st) return st;
-        g2.a = hc;
-        g2.a_scales = hs;
+        g2.a = hq;
         g2.a_global = t->a2_scale;
     } else {
         g2.a = h;
     }
-    st = hip_status(launch_gemm(g2, af, Epi::kMoeDown, Tile::k128x128, grid_m, s), "moe gemm2");
+    st = hip_status(launch_gemm_a16(g2, af, Epi::kMoeDown, tile, grid_m, s), "moe gemm2");
     if (st) return st;
     return hip_status(launch_moe_combine(Y, inv, t->topk_weights, p->T, (int32_t)p->top_k, p->H, t->out, s),
                       "moe combine");

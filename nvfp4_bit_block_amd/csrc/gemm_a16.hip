@@ -118,12 +118,24 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     const int wm = wave / WN, wn = wave % WN;
     const int c32 = lane & 31, hf = lane >> 5;
 
-    // ---- tile, group and K range of this workgroup
+    // ---- tile, group and K range of this workgroup.  Workgroups are dealt to
+    // the 8 XCDs round-robin by linear id; the id is renumbered so that each
+    // XCD receives a contiguous run of tiles.  Grouped problems walk the
+    // column tiles of one row tile consecutively (they share the row tile's
+    // activations in that XCD's L2); ungrouped ones walk bands of kGroupM row
+    // tiles so that concurrent tiles share both operands.
+    const int nwg = (int)gridDim.x;
+    int id = (int)blockIdx.x;
+    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
     int grp = 0, tn, kz;
     int64_t row_beg, row_end;
     if (g.groups > 0) {
-        const int mt = (int)blockIdx.y;
-        if (mt >= g.tile_off[g.groups]) return;
+        const int ntiles = g.grouped_ntiles, mtiles = g.grouped_mtiles;
+        kz = id / (ntiles * mtiles);
+        const int t = id - kz * ntiles * mtiles;
+        const int mt = t / ntiles;
+        tn = t - mt * ntiles;
+        if (kz >= g.ksplit || mt >= g.tile_off[g.groups]) return;
         int lo = 0, hi = g.groups;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -132,16 +144,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
         grp = lo;
         row_beg = (int64_t)g.row_off[grp] + (int64_t)(mt - g.tile_off[grp]) * BM;
         row_end = min((int64_t)g.row_off[grp + 1], row_beg + BM);
-        tn = (int)blockIdx.x;
-        kz = (int)blockIdx.z;
     } else {
-        // Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber
-        // so that each XCD receives a contiguous run of tiles, and walk tiles in
-        // bands of kGroupM m-tiles so that concurrently running tiles share rows
-        // of A and columns of B in that XCD's L2.
-        const int nwg = (int)gridDim.x;
-        int id = (int)blockIdx.x;
-        if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
         const int mtiles = (int)((g.M + BM - 1) / BM);
         const int ntiles = (int)((g.N + BN - 1) / BN);
         const int per_split = mtiles * ntiles;
@@ -262,7 +265,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     // are requested before the MFMAs of group kk are issued (the scheduling
     // barriers keep that order; left alone, the scheduler re-reads fragments
     // just in time to save registers and the MFMAs wait on LDS latency).
+    // Waves whose rows all lie past the end of the row tile (a group's last,
+    // partly filled tile) skip their MFMAs; the copy work stays shared.
+    const bool wave_rows = (int64_t)wm * WTM < row_end - row_beg;
     auto compute_step = [&](int buf) {
+        if (!wave_rows) return;
         const uint8_t* base = smem + buf * C::STAGE;
         uint4 cb[TN];
         f32x2 sb[TN];
@@ -352,18 +359,22 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
 }
 
 template <int TM, int TN, int WM, int WN, AFmt AF, Epi EP>
-hipError_t launch_cfg(const GemmArgs& g, int grid_m, hipStream_t stream) {
+hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     using C = Cfg<TM, TN, WM, WN>;
-    dim3 grid;
+    GemmArgs g = g0;
+    int64_t wgs;
     if (g.groups > 0) {
+        // grid_m bounds the row tiles of all groups; surplus workgroups exit
         const int64_t ncols = (EP == Epi::kMoeGateUp) ? g.half_n : g.N;
         const int64_t bn = (EP == Epi::kMoeGateUp) ? C::BN / 2 : C::BN;
-        grid = dim3((unsigned)((ncols + bn - 1) / bn), (unsigned)grid_m, (unsigned)g.ksplit);
+        g.grouped_ntiles = (int32_t)((ncols + bn - 1) / bn);
+        g.grouped_mtiles = grid_m;
+        wgs = (int64_t)g.grouped_ntiles * grid_m * g.ksplit;
+        wgs = (wgs + 7) / 8 * 8;  // a multiple of 8 for the XCD renumbering
     } else {
-        const int64_t tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
-        grid = dim3((unsigned)tiles);
+        wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, AF, EP>), grid, dim3(C::NT), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, AF, EP>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
 }
 

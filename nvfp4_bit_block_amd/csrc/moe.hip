@@ -2,7 +2,7 @@
 // layer ("GLM-5.2-NVFP4" model card: 256 routed experts, 8 per token).
 //
 // Routing ids and gate weights are inputs.  One workgroup counts the slots per
-// expert, scans the counts into row offsets and 128-row tile offsets, and
+// expert, scans the counts into row offsets and bm-row tile offsets, and
 // scatters every (token, slot) into its expert's contiguous rows.  The row a
 // slot lands on may differ from run to run (LDS atomics), but every row is
 // computed on its own, so the layer output does not depend on it.  The
