@@ -35,6 +35,105 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA
 FP4_PEAK_TFLOPS = 10066.0      # dense MXFP4 (context only)
 METRIC = "NVFP4 bs1 GEMV HBM TB/s; W4A4 GEMM/MoE TFLOPS; % of roofline"
+TRAFFIC_FILE = "profiles/gemv_w4a16_o_proj_M1_hbm_traffic.md"
+COPY_BYTES = 512 << 20
+# sources of the kernel the traffic figure belongs to: a change to any of
+# them voids the recorded figure
+TRAFFIC_SOURCES = ("nvfp4_bit_block_amd/csrc/gemv.hip", "nvfp4_bit_block_amd/csrc/nvfp4_device.hpp")
+
+
+def _sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe():
+    import torch
+    import nvfp4_bit_block_amd as nv
+    import workloads as wl
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    w, x = wl.gemv_inputs("o_proj")
+    c, s, g = nv.quantize(torch.from_numpy(w.view(np.int16)).to(dev))
+    x1 = torch.from_numpy(np.ascontiguousarray(x[:1]).view(np.int16)).to(dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    for _ in range(3):
+        nv.gemv_w4a16(x1, c, s, g)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+
+
+def _counter_per_dispatch(db, counter):
+    import sqlite3
+    con = sqlite3.connect(db)
+    q = ("select dispatch_id, kernel_name, sum(value) from counters_collection "
+         "where counter_name = ? group by dispatch_id order by dispatch_id")
+    return [(k, v) for _, k, v in con.execute(q, (counter,))]
+
+
+def traffic_parse(fetch_db, write_db):
+    """Scale each counter by its reading for the copy of COPY_BYTES (read
+    once, written once) and record the GEMV's HBM bytes per launch."""
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = _counter_per_dispatch(db, counter)
+        copy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+        gemv = [v for k, v in rows if "k_gemv" in k]
+        if not copy or not gemv:
+            raise SystemExit(f"{db}: no copy or GEMV dispatch with {counter}")
+        factor = COPY_BYTES / (float(np.median(copy)) * 1024.0)
+        out[counter] = {"copy_kib": float(np.median(copy)), "factor": factor,
+                        "gemv_kib": float(np.median(gemv)), "gemv_bytes": float(np.median(gemv)) * 1024.0 * factor}
+    algo = 6144 * 16384 // 2 + 6144 * 16384 // 16
+    total = out["FETCH_SIZE"]["gemv_bytes"] + out["WRITE_SIZE"]["gemv_bytes"]
+    rec = {"kernel": "k_gemv<1> batch-1 o_proj 6144x16384", "sources_sha256_16": _sources_digest(),
+           "fetch_bytes": round(out["FETCH_SIZE"]["gemv_bytes"]), "write_bytes": round(out["WRITE_SIZE"]["gemv_bytes"]),
+           "traffic_bytes": round(total), "algorithmic_bytes": algo}
+    lines = [
+        "# HBM traffic: batch-1 W4A16 GEMV, o_proj 6144 x 16384", "",
+        "Commands (repository root on the MI355X box; two counter passes, then this file):", "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch -o run -- "
+        "python3 $REPO/bench.py --traffic-probe",
+        "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write -o run -- "
+        "python3 $REPO/bench.py --traffic-probe",
+        "python3 bench.py --traffic-parse gpurun_out/pmc_fetch/run_results.db gpurun_out/pmc_write/run_results.db",
+        "```", "",
+        f"Each counter is scaled by bytes / counter for a plain {COPY_BYTES >> 20} MiB device copy "
+        "(torch copy_: the same bytes read and written), medians over three dispatches.", "",
+        "| counter | copy (KiB) | scale | GEMV (KiB) | GEMV bytes |", "|---|---|---|---|---|",
+    ]
+    for ctr, d in out.items():
+        lines.append(f"| {ctr} | {d['copy_kib']:.0f} | {d['factor']:.4f} | {d['gemv_kib']:.0f} | {d['gemv_bytes']:.0f} |")
+    lines += ["", f"Algorithmic bytes per launch (codes + scales): {algo}; measured HBM traffic per launch: "
+              f"{total:.0f} ({total / algo:.3f} x).", "",
+              "traffic-json: " + json.dumps(rec)]
+    with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the batch-1 o_proj GEMV from the committed
+    counter summary, or None when it is missing or the kernel changed."""
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_FILE)) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("sources_sha256_16") == _sources_digest():
+                        return rec
+    except OSError:
+        pass
+    return None
 
 
 def parse():
@@ -45,6 +144,11 @@ def parse():
     ap.add_argument("--rows", default="all", help="comma list of row groups: quant,gemv,gemm,moe or all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch a plain 512 MiB copy and the batch-1 o_proj GEMV, three times each "
+                         "(run this under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--traffic-parse", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="turn the two rocprofv3 databases of --traffic-probe into " + TRAFFIC_FILE)
     return ap.parse_args()
 
 
@@ -68,6 +172,12 @@ class Row:
 
 def main():
     args = parse()
+    if args.traffic_parse:
+        traffic_parse(*args.traffic_parse)
+        return
+    if args.traffic_probe:
+        traffic_probe()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs the NVFP4 path on exactly one GPU; --gpus {args.gpus} "
@@ -269,9 +379,12 @@ def main():
     value = head["GB_s"] / 1e3 if head else None
     roofline = None
     if head:
+        tr = recorded_traffic()
         roofline = {"kernel": "k_gemv<1> (nvfp4_gemv_w4a16, o_proj 6144x16384, M=1)", "bound": "hbm",
                     "achieved": head["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(head["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(head["GB_s"] / HBM_PEAK_GBS, 4),
+                    "traffic": None if tr is None else tr["traffic_bytes"],
+                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled; " + TRAFFIC_FILE + ")",
                     "bytes_per_launch": 6144 * 16384 // 2 + 6144 * 16384 // 16,
                     "us_per_launch": head["us_per_launch"]}
     progress("timed steps done")

@@ -44,7 +44,9 @@ struct GemmPlan {
 // and splits K to spread that stream over the chip).
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
-    if (M <= 8) {
+    // The VALU GEMV wins while its activation slice fits in registers (M <= 4
+    // or short rows); beyond that the MFMA tiles are faster.
+    if (M <= 4 || (M <= 8 && K <= 4096)) {
         p.gemv = true;
         return p;
     }
@@ -63,7 +65,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 // Rows of the activation handled per GEMM launch: the kernel addresses the
 // decoded activation through one buffer resource, which spans < 2 GiB.
 int64_t gemm_chunk_rows(int64_t M, int64_t K) {
-    int64_t cap = (kRdMaxBytes - 1) / (K * 2);
+    int64_t cap = (kMaxOperandBytes - 1) / (K * 2);
     if (cap >= 256) cap = cap / 256 * 256;
     return cap < M ? cap : M;
 }
@@ -236,7 +238,7 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
         return fail(NVFP4_ERR_SHAPE, "gemm: need M, N >= 0, K > 0 and K %% 16 == 0%s");
     if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm: K must be a multiple of 64%s");
-    if (M > 8 && ((int64_t)N * (K / 2) >= kRdMaxBytes || gemm_chunk_rows(M, K) < 1))
+    if (!plan_gemm(M, N, K).gemv && ((int64_t)N * (K / 2) >= kMaxOperandBytes || gemm_chunk_rows(M, K) < 1))
         return fail(NVFP4_ERR_UNSUPPORTED, "gemm: weight matrix of 2 GiB or more%s");
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!x || !input_scale || !w_codes || !w_scales || !w_global || !y)
@@ -320,8 +322,8 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         // the GEMM kernels address each operand through one buffer resource
         const int64_t S = p->T * p->top_k;
         const int64_t act = p->mode == 1 ? S * p->H * 2 : p->T * p->H * 2;
-        if (act >= kRdMaxBytes || S * p->I * 2 >= kRdMaxBytes || 2 * p->I * (p->H / 2) >= kRdMaxBytes ||
-            p->H * (p->I / 2) >= kRdMaxBytes)
+        if (act >= kMaxOperandBytes || S * p->I * 2 >= kMaxOperandBytes || 2 * p->I * (p->H / 2) >= kMaxOperandBytes ||
+            p->H * (p->I / 2) >= kMaxOperandBytes)
             return fail(NVFP4_ERR_UNSUPPORTED, "moe: an operand of 2 GiB or more%s");
     }
     if (p->T == 0) return NVFP4_OK;

@@ -105,7 +105,7 @@ struct Cfg {
     static_assert(2 * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int TM, int TN, int WM, int WN, AFmt AF, Epi EP>
+template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN>;
     using Op = typename OpOf<AF>::T;
@@ -223,23 +223,28 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     }
     const uint32_t lbs = C::A_BYTES + C::BC_BYTES + 4 * (tid < BN ? tid : 0);
 
-    uint4 ra_st[C::A_PER_T], rb_st[C::B_PER_T];
-    uint32_t rs_st = 0;
-    auto load_step = [&](int kc) {
-#pragma unroll
-        for (int u = 0; u < C::A_PER_T; ++u) ra_st[u] = bload16(ra, va[u], (uint32_t)kc * 128u);
-#pragma unroll
-        for (int u = 0; u < C::B_PER_T; ++u) rb_st[u] = bload16(rb_c, vbc[u], (uint32_t)kc * 32u);
-        rs_st = bload4(rb_s, vbs, (uint32_t)kc * 4u);
+    // PD register sets, each holding one step's share of the copy: step t
+    // lives in set t % PD, so the loads of PD steps are in flight at once.
+    struct StageRegs {
+        uint4 a[C::A_PER_T], b[C::B_PER_T];
+        uint32_t s;
     };
-    auto store_step = [&](int buf) {
+    StageRegs stg[PD];
+    auto load_step = [&](StageRegs& r, int kc) {
+#pragma unroll
+        for (int u = 0; u < C::A_PER_T; ++u) r.a[u] = bload16(ra, va[u], (uint32_t)kc * 128u);
+#pragma unroll
+        for (int u = 0; u < C::B_PER_T; ++u) r.b[u] = bload16(rb_c, vbc[u], (uint32_t)kc * 32u);
+        r.s = bload4(rb_s, vbs, (uint32_t)kc * 4u);
+    };
+    auto store_step = [&](const StageRegs& r, int buf) {
         uint8_t* base = smem + buf * C::STAGE;
 #pragma unroll
-        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la[u]) = ra_st[u];
+        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la[u]) = r.a[u];
 #pragma unroll
         for (int u = 0; u < C::B_PER_T; ++u)
-            if (tid + C::NT * u < C::B_CHUNKS) *reinterpret_cast<uint4*>(base + lbc[u]) = rb_st[u];
-        if (tid < BN) *reinterpret_cast<uint32_t*>(base + lbs) = rs_st;
+            if (tid + C::NT * u < C::B_CHUNKS) *reinterpret_cast<uint4*>(base + lbc[u]) = r.b[u];
+        if (tid < BN) *reinterpret_cast<uint32_t*>(base + lbs) = r.s;
     };
 
     // ---- fragment addresses within a stage buffer
@@ -301,24 +306,35 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
         }
     };
 
-    // ---- main loop, one barrier per step: iteration s multiplies buffer s % 2
-    // while the loads of step s + 1 are in flight, then stores step s + 1 into
-    // the other buffer (last read in iteration s - 1, before the previous
-    // barrier) and starts the loads of step s + 2.
+    // ---- main loop, one barrier per step: iteration s multiplies LDS buffer
+    // s % 2, then writes step s + 1 from its register set into the other
+    // buffer (last read in iteration s - 1, before the previous barrier) and
+    // refills that set with step s + 1 + PD.  Loads past the last step re-read
+    // it (the clamp keeps the load count per iteration fixed, so the waits
+    // stay exact); their data is never multiplied.
     if (nsteps > 0) {
-        load_step(kc0);
-        store_step(0);
-        if (nsteps > 1) load_step(kc0 + 1);
+#pragma unroll
+        for (int u = 0; u < PD; ++u) load_step(stg[u], kc0 + min(u, nsteps - 1));
+        store_step(stg[0], 0);
+        load_step(stg[0], kc0 + min(PD, nsteps - 1));
         __syncthreads();
     }
-    for (int s = 0; s < nsteps; ++s) {
+    auto step = [&](int s, StageRegs& next) {
         compute_step(s & 1);
-        if (s + 1 < nsteps) {
-            store_step((s + 1) & 1);
-            if (s + 2 < nsteps) load_step(kc0 + s + 2);
-        }
+        store_step(next, (s + 1) & 1);
+        load_step(next, kc0 + min(s + 1 + PD, nsteps - 1));
         __syncthreads();
+    };
+    // whole groups of PD steps without conditions (exact wait counts), then
+    // the remaining steps
+    const int nmain = nsteps / PD * PD;
+    for (int s0 = 0; s0 < nmain; s0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) step(s0 + u, stg[(u + 1) % PD]);
     }
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+        if (nmain + u < nsteps) step(nmain + u, stg[(u + 1) % PD]);
 
     // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32
     const int gi = g.groups > 0 ? grp : 0;
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     }
 }
 
-template <int TM, int TN, int WM, int WN, AFmt AF, Epi EP>
+template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP>
 hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     using C = Cfg<TM, TN, WM, WN>;
     GemmArgs g = g0;
@@ -374,24 +390,38 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     } else {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, AF, EP>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, PD, AF, EP>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
 }
 
 template <AFmt AF, Epi EP>
 hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t stream) {
     switch (tile) {
-        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, AF, EP>(g, grid_m, stream);
-        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
+        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// Split-K finish: y = bf16(scale * sum_s partial[s]) with the splits summed
+// in order.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial, int ksplit,
+                                                       int64_t M, int64_t N, const float* __restrict__ g0,
+                                                       const float* __restrict__ g1, uint16_t* __restrict__ y) {
+    const float scale = *g0 * (g1 ? *g1 : 1.0f);
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        float s = 0.0f;
+        for (int k = 0; k < ksplit; ++k) s += partial[(int64_t)k * total + i];
+        y[i] = (uint16_t)f32_to_bf16_rne(s * scale);
+    }
 }
 
 }  // namespace
@@ -442,6 +472,16 @@ hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, 
     }
 #undef NVFP4_EPI
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
+                                const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
+    int64_t grid = (M * N + 255) / 256;
+    if (grid > 8192) grid = 8192;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)grid), dim3(256), 0, stream, partial, ksplit, M, N, g0, g1,
+                       y);
+    return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -62,9 +62,9 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, con
 
 // -------------------------------------------------------------------- GEMM --
 
-// A operand formats: bf16 values, NVFP4 codes + scales, or f16 values that
-// are already the exact products q * s of an NVFP4 encoding.
-enum class AFmt : int { kBf16 = 0, kFp4 = 1, kF16 = 2 };
+// A operand formats: bf16 values, or f16 values that are the exact products
+// q * s of an NVFP4 encoding.
+enum class AFmt : int { kBf16 = 0, kF16 = 2 };
 enum class Epi : int {
     kStoreBf16 = 0,   // y = bf16(acc * scale)
     kPartialF32 = 1,  // partial[split] = acc (split-K, reduced later)
@@ -73,9 +73,8 @@ enum class Epi : int {
 };
 
 struct GemmArgs {
-    // A operand: bf16 [*, K] rows (optionally gathered) or NVFP4 codes/scales.
+    // A operand: 16-bit [*, K] rows (optionally gathered).
     const void* a = nullptr;
-    const uint8_t* a_scales = nullptr;
     const int32_t* a_rows = nullptr;  // bf16 gather: A row of output row r = a_rows[r] / a_div
     int32_t a_div = 1;
     int64_t a_src_rows = 0;           // bf16 A: rows of the source tensor
@@ -98,45 +97,6 @@ struct GemmArgs {
     int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
 };
 
-// Tile shapes: block rows x block cols.
-enum class Tile : int { k128x128 = 0, k64x128 = 1, k32x128 = 2 };
-
-hipError_t launch_gemm(const GemmArgs& g, AFmt afmt, Epi epi, Tile tile, int grid_m,
-                       hipStream_t stream);
-
-// Register-direct GEMM tiles (gemm_rd.hip): workgroup tile rows x cols and
-// the per-wave tile.
-enum class RdTile : int {
-    k128x128_w64x64 = 0,
-    k256x128_w128x64 = 1,
-    k128x256_w64x128 = 2,
-    k256x256_w128x128 = 3,
-    k128x128_w128x32 = 4,
-    k128x256_w128x64 = 5,
-    k64x128_w64x32 = 6,
-    k32x128_w32x32 = 7,
-};
-int rd_tile_rows(RdTile t);
-int rd_tile_cols(RdTile t);
-
-// Byte ranges each operand buffer of launch_gemm_rd must stay below.
-constexpr int64_t kRdMaxBytes = (int64_t)1 << 31;
-
-hipError_t launch_gemm_rd(const GemmArgs& g, AFmt afmt, Epi epi, RdTile tile, int grid_m,
-                          hipStream_t stream);
-
-// LDS-staged W4A4 GEMM tiles (gemm_st.hip; NVFP4 A and B, K % 256 == 0).
-enum class StTile : int {
-    k256x256_w128x128 = 0,
-    k256x256_w128x64 = 1,
-    k256x128_w128x64 = 2,
-    k128x256_w128x64 = 3,
-    k128x128_w64x64 = 4,
-};
-int st_tile_rows(StTile t);
-int st_tile_cols(StTile t);
-hipError_t launch_gemm_st(const GemmArgs& g, Epi epi, StTile tile, int grid_m, hipStream_t stream);
-
 // GEMM tiles with a 16-bit A operand (gemm_a16.hip): f16 products q * s
 // (W4A4) or bf16 activations (W4A16); NVFP4 B.  Workgroup tile rows x cols
 // and the per-wave tile.
@@ -152,6 +112,9 @@ enum class A16Tile : int {
     k32x256_w32x64 = 8,
 };
 int a16_tile_rows(A16Tile t);
+// Each operand of launch_gemm_a16 is addressed through one buffer resource
+// and must span fewer bytes than this.
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
 int a16_tile_cols(A16Tile t);
 hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, int grid_m,
                            hipStream_t stream);
