@@ -121,6 +121,29 @@ def traffic_parse(fetch_db, write_db):
     print(json.dumps(rec))
 
 
+def trace_summary(db, filt):
+    """Per-kernel durations from a rocprofv3 kernel-trace database, one row per
+    kernel and launch shape, sorted by total time."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    q = ("select name, grid_x, workgroup_x, count(*), avg(duration) / 1000.0, min(duration) / 1000.0, "
+         "max(duration) / 1000.0, sum(duration) / 1000.0, vgpr_count, accum_vgpr_count, lds_size, scratch_size "
+         "from kernels group by name, grid_x, grid_y, grid_z order by sum(duration) desc")
+    print("| kernel | grid (work-items) | wg | launches | avg us | min us | max us | total us | VGPR | AGPR | LDS B | scratch B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in con.execute(q):
+        name = r[0]
+        if "nvfp4::" not in name or (filt and filt not in name):
+            continue
+        short = name.replace("(anonymous namespace)::", "").replace("nvfp4::", "")
+        if short.startswith("void "):        # a template instantiation: keep its arguments
+            short = short[5:].split(">(")[0] + ">"
+        else:
+            short = short.split("(")[0]
+        print(f"| `{short[:100]}` | {r[1]} | {r[2]} | {r[3]} | {r[4]:.2f} | {r[5]:.2f} | {r[6]:.2f} | {r[7]:.0f} | "
+              f"{r[8]} | {r[9]} | {r[10]} | {r[11]} |")
+
+
 def recorded_traffic():
     """HBM bytes per launch of the batch-1 o_proj GEMV from the committed
     counter summary, or None when it is missing or the kernel changed."""
@@ -147,6 +170,9 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch a plain 512 MiB copy and the batch-1 o_proj GEMV, three times each "
                          "(run this under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "FILTER"),
+                    help="print a markdown table of a rocprofv3 --kernel-trace database (kernels whose name "
+                         "contains FILTER; '' for all library kernels)")
     ap.add_argument("--traffic-parse", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn the two rocprofv3 databases of --traffic-probe into " + TRAFFIC_FILE)
     return ap.parse_args()
@@ -174,6 +200,9 @@ def main():
     args = parse()
     if args.traffic_parse:
         traffic_parse(*args.traffic_parse)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.traffic_probe:
         traffic_probe()

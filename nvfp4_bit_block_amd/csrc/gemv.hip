@@ -300,97 +300,6 @@ __global__ __launch_bounds__(THREADS) void k_gemv_any(const uint16_t* __restrict
     }
 }
 
-// Whole rows per wave, activation in LDS: K == NCH * 2048.  A wave owns RW
-// rows at a time; lane l holds chunks l + 64 j (j < NCH) of each, so every
-// load instruction reads 1 KB of contiguous codes and a wave has RW * NCH KB
-// of codes in flight.  Two register sets are used in turn: the loads of the
-// next batch are issued before the current one is multiplied.  No
-// cross-wave reduction is needed (a wave finishes its rows), so the waves of
-// a workgroup only meet once, after staging the activation.
-template <int M, int NCH, int RW>
-__global__ __launch_bounds__(kThreads) void k_gemv_rows(const uint16_t* __restrict__ x, int64_t N,
-                                                        int64_t K, const uint8_t* __restrict__ wc,
-                                                        const uint8_t* __restrict__ ws,
-                                                        const float* __restrict__ g0,
-                                                        const float* __restrict__ g1,
-                                                        uint16_t* __restrict__ y) {
-    extern __shared__ uint4 xlds[];
-    constexpr int kWavesPerBlock = kThreads / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t KB = K / 2, KS16 = K / 16, nchunk = K / 32;
-    const int64_t nbatch = (N + RW - 1) / RW;
-    const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-
-    auto load = [&](Frag<RW, NCH>& f, int64_t b) {
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int64_t row = min(b * RW + r, N - 1);
-            const uint8_t* wrow = wc + row * KB;
-            const uint16_t* srow = reinterpret_cast<const uint16_t*>(ws + row * KS16);
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                f.q[r][j] = load_nt16(wrow + (lane + 64 * j) * 16);
-                f.s[r][j] = __builtin_nontemporal_load(srow + lane + 64 * j);
-            }
-        }
-    };
-    Frag<RW, NCH> fa, fb;
-    if (wid < nbatch) load(fa, wid);
-    stage_x_lds<M, kThreads>(xlds, x, K);
-    const float scale = *g0 * (g1 ? *g1 : 1.0f);
-
-    auto run = [&](const Frag<RW, NCH>& f, int64_t b) {
-        float acc[RW][M] = {};
-        // (one chunk at a time: the scheduling barriers stop the activation
-        // reads of later chunks from being hoisted, which would hold them all
-        // in registers at once)
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                chunk_dot<M>(f.q[r][j], f.s[r][j],
-                             [&](int m, int i) { return xlds[(m * 4 + i) * nchunk + lane + 64 * j]; },
-                             acc[r]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = wave_sum_lane63(acc[r][m]);
-        if (lane == kWave - 1) {
-#pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                if (b * RW + r >= N) break;
-#pragma unroll
-                for (int m = 0; m < M; ++m) y[m * N + b * RW + r] = (uint16_t)f32_to_bf16_rne(acc[r][m] * scale);
-            }
-        }
-    };
-    // batches wid, wid + nw, ...: a-set holds even steps, b-set odd ones; the
-    // next batch's loads are clamped to a valid row when past the end
-    for (int64_t b = wid; b < nbatch; b += 2 * nw) {
-        load(fb, min(b + nw, nbatch - 1));
-        run(fa, b);
-        if (b + nw >= nbatch) break;
-        load(fa, min(b + 2 * nw, nbatch - 1));
-        run(fb, b + nw);
-    }
-}
-
-template <int M, int NCH, int RW>
-hipError_t launch_rows(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
-                       const float* g0, const float* g1, uint16_t* y, hipStream_t stream, int blocks_per_cu) {
-    constexpr int64_t waves = kThreads / kWave;
-    const int64_t nbatch = (N + RW - 1) / RW;
-    int64_t grid = min((int64_t)256 * blocks_per_cu, (nbatch + waves - 1) / waves);
-    if (grid < 1) grid = 1;
-    const size_t lds = (size_t)M * (size_t)K * 2;
-    hipLaunchKernelGGL((k_gemv_rows<M, NCH, RW>), dim3((unsigned)grid), dim3(kThreads), lds, stream, x, N, K, wc,
-                       ws, g0, g1, y);
-    return hipGetLastError();
-}
-
 constexpr int64_t kMaxLdsBytes = 64 * 1024;
 
 // Grid: about `blocks_per_cu` workgroups per CU on a 256-CU chip, never
