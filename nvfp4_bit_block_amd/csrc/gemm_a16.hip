@@ -120,22 +120,30 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
 
     // ---- tile, group and K range of this workgroup.  Workgroups are dealt to
     // the 8 XCDs round-robin by linear id; the id is renumbered so that each
-    // XCD receives a contiguous run of tiles.  Grouped problems walk the
-    // column tiles of one row tile consecutively (they share the row tile's
-    // activations in that XCD's L2); ungrouped ones walk bands of kGroupM row
-    // tiles so that concurrent tiles share both operands.
+    // XCD receives a contiguous run of the real tiles (a grouped launch is
+    // sized for the worst case: its surplus workgroups hold ids past the real
+    // tile count, read from tile_off on the device, and exit).  Grouped
+    // problems walk the column tiles of one row tile consecutively (they share
+    // the row tile's activations in that XCD's L2); ungrouped ones walk bands
+    // of kGroupM row tiles so that concurrent tiles share both operands.
     const int nwg = (int)gridDim.x;
+    const int gm_tiles = g.groups > 0 ? g.tile_off[g.groups] : 0;
+    const int total = g.groups > 0 ? gm_tiles * g.grouped_ntiles * g.ksplit : nwg;
     int id = (int)blockIdx.x;
-    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+    if ((nwg & 7) == 0) {
+        const int per_xcd = (total + 7) >> 3, j = id >> 3;
+        if (j >= per_xcd) return;
+        id = (id & 7) * per_xcd + j;
+    }
+    if (id >= total) return;
     int grp = 0, tn, kz;
     int64_t row_beg, row_end;
     if (g.groups > 0) {
-        const int ntiles = g.grouped_ntiles, mtiles = g.grouped_mtiles;
-        kz = id / (ntiles * mtiles);
-        const int t = id - kz * ntiles * mtiles;
+        const int ntiles = g.grouped_ntiles;
+        kz = id / (ntiles * gm_tiles);
+        const int t = id - kz * ntiles * gm_tiles;
         const int mt = t / ntiles;
         tn = t - mt * ntiles;
-        if (kz >= g.ksplit || mt >= g.tile_off[g.groups]) return;
         int lo = 0, hi = g.groups;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -384,7 +392,6 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
         const int64_t ncols = (EP == Epi::kMoeGateUp) ? g.half_n : g.N;
         const int64_t bn = (EP == Epi::kMoeGateUp) ? C::BN / 2 : C::BN;
         g.grouped_ntiles = (int32_t)((ncols + bn - 1) / bn);
-        g.grouped_mtiles = grid_m;
         wgs = (int64_t)g.grouped_ntiles * grid_m * g.ksplit;
         wgs = (wgs + 7) / 8 * 8;  // a multiple of 8 for the XCD renumbering
     } else {

@@ -71,15 +71,30 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
          i += (int64_t)gridDim.x * 256) {
         const int64_t t = i / h4, c = (i - t * h4) * 4;
         float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-        for (int j = 0; j < topk; ++j) {
-            const int32_t pos = inv[t * topk + j];
-            if (pos < 0) continue;
-            const float wj = w[t * topk + j];
-            const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)pos * H + c);
-            s0 = __builtin_fmaf(wj, v.x, s0);
-            s1 = __builtin_fmaf(wj, v.y, s1);
-            s2 = __builtin_fmaf(wj, v.z, s2);
-            s3 = __builtin_fmaf(wj, v.w, s3);
+        // slots in order, eight at a time: all eight row loads are issued
+        // before the first sum (dropped slots load row 0 and are not added)
+        for (int j0 = 0; j0 < topk; j0 += 8) {
+            int32_t pos[8];
+            float wj[8];
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool in = j0 + u < topk;
+                pos[u] = in ? inv[t * topk + j0 + u] : -1;
+                wj[u] = in ? w[t * topk + j0 + u] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(Y + (int64_t)(pos[u] < 0 ? 0 : pos[u]) * H + c));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (pos[u] < 0) continue;
+                s0 = __builtin_fmaf(wj[u], v[u][0], s0);
+                s1 = __builtin_fmaf(wj[u], v[u][1], s1);
+                s2 = __builtin_fmaf(wj[u], v[u][2], s2);
+                s3 = __builtin_fmaf(wj[u], v[u][3], s3);
+            }
         }
         const uint32_t lo = f32_to_bf16_rne(s0) | (f32_to_bf16_rne(s1) << 16);
         const uint32_t hi = f32_to_bf16_rne(s2) | (f32_to_bf16_rne(s3) << 16);

@@ -89,7 +89,7 @@ struct GemmArgs {
     const int32_t* row_off = nullptr;
     const int32_t* tile_off = nullptr;
     int32_t groups = 0;
-    int32_t grouped_ntiles = 0, grouped_mtiles = 0;  // set by the launcher
+    int32_t grouped_ntiles = 0;  // set by the launcher
     // output
     void* out = nullptr;
     int64_t ldo = 0;
