@@ -123,7 +123,7 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
  * (same arithmetic as nvfp4_quantize in static mode), then
  * y[m, n] = bf16( input_scale * Sg_w * sum_b sx[m,b] sw[n,b] sum_{k in b} qx qw ),
  * fp32 accumulation.  w_* as in the GEMV; y bf16 [M, N].  K % 64 == 0, and
- * unless M <= 4 (or M <= 8 with K <= 4096) the weight codes must span less
+ * unless M <= 4 (or M <= 8 with K <= 4096 or K == 16384) the weight codes must span less
  * than 2 GiB (N * K / 2 < 2^31); else UNSUPPORTED.  Workspace: nvfp4_gemm_w4a4_workspace_size(M, N, K)
  * bytes (the quantized X, held as its exact products q * s in 16-bit form,
  * and, for small M, split-K partial sums).

@@ -44,9 +44,10 @@ struct GemmPlan {
 // and splits K to spread that stream over the chip).
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
-    // The VALU GEMV wins while its activation slice fits in registers (M <= 4
-    // or short rows); beyond that the MFMA tiles are faster.
-    if (M <= 4 || (M <= 8 && K <= 4096)) {
+    // The VALU GEMV wins while its activation slice fits in registers (M <= 4,
+    // the K = 2048 and 16384 layouts up to M = 8) or in LDS (short rows);
+    // beyond that the MFMA tiles are faster.
+    if (M <= 4 || (M <= 8 && (K <= 4096 || K == 16384))) {
         p.gemv = true;
         return p;
     }

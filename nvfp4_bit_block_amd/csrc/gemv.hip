@@ -92,8 +92,8 @@ struct Frag {
     uint32_t s[RW][NCH];
 };
 
-// Fixed chunk layout: K == KS * NCH * 2048.  A workgroup of 4 waves forms
-// 4/KS row groups of KS waves; the KS waves of a group split K (wave part p
+// Fixed chunk layout: K == KS * NCH * 2048.  A workgroup of THREADS / 64
+// waves forms row groups of KS waves; the KS waves of a group split K (wave part p
 // owns chunks p*64*NCH + lane + 64*j, j < NCH), so each lane keeps only its
 // NCH chunks of the activation in VGPRs.  A row group walks its batches of RW
 // rows with one fragment of registers: the registers of chunk j are refilled
@@ -102,14 +102,14 @@ struct Frag {
 // refill is unconditional (no register copies).  Partial row sums are reduced
 // across the wave with shuffles and, when KS > 1, across the group's waves
 // through LDS.
-template <int M, int NCH, int KS, int RW, bool CONTIG = false>
-__global__ __launch_bounds__(kThreads) void k_gemv(const uint16_t* __restrict__ x, int64_t N,
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads>
+__global__ __launch_bounds__(THREADS) void k_gemv(const uint16_t* __restrict__ x, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ wc,
                                                    const uint8_t* __restrict__ ws,
                                                    const float* __restrict__ g0,
                                                    const float* __restrict__ g1,
                                                    uint16_t* __restrict__ y) {
-    constexpr int kWavesPerBlock = kThreads / kWave;
+    constexpr int kWavesPerBlock = THREADS / kWave;
     constexpr int kGroups = kWavesPerBlock / KS;
     static_assert(kWavesPerBlock % KS == 0, "row groups");
     __shared__ float red[2][kWavesPerBlock][RW][M];
@@ -118,11 +118,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint16_t* __restrict__ 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int grp = wave / KS, part = wave % KS;
     const int64_t KB = K / 2, KS16 = K / 16;
-    // chunk of (lane, j): interleaved (lane + 64 j: every load instruction of
-    // the wave reads 1 KB contiguous) or, with CONTIG, lane-contiguous
-    // (NCH * lane + j: a lane's scale bytes are adjacent and come in one load)
+    // chunk of (lane, j): lane + 64 j of the part, so every load instruction
+    // of the wave reads 1 KB contiguous
     const int64_t cbase = (int64_t)part * 64 * NCH;
-    auto chunk = [&](int j) -> int64_t { return CONTIG ? cbase + NCH * lane + j : cbase + lane + 64 * j; };
+    auto chunk = [&](int j) -> int64_t { return cbase + lane + 64 * j; };
 
     // batches of RW rows: this group owns b = gid, gid + ngroups, ...
     const int64_t nbatch = (N + RW - 1) / RW;
@@ -132,31 +131,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint16_t* __restrict__ 
     // reduction synchronizes them); batches past the end are computed on a
     // clamped row and not stored
     const int64_t iters = (nbatch + ngroups - 1) / ngroups;
-    const int64_t blk_first = (int64_t)blockIdx.x * kGroups;
     const int64_t my_iters = (KS > 1) ? iters : (gid < nbatch ? (nbatch - 1 - gid) / ngroups + 1 : 0);
-    (void)blk_first;
 
     // one row's chunks and scale pairs into fragment slot r
     auto load_row = [&](Frag<RW, NCH>& f, int r, const uint8_t* wrow, const uint16_t* srow) {
-        if constexpr (CONTIG) {
-            static_assert(NCH == 2 || NCH == 4, "contiguous scale load");
 #pragma unroll
-            for (int j = 0; j < NCH; ++j) f.q[r][j] = *reinterpret_cast<const uint4*>(wrow + chunk(j) * 16);
-            if constexpr (NCH == 2) {
-                const uint32_t sw = *reinterpret_cast<const uint32_t*>(srow + chunk(0));
-                f.s[r][0] = sw & 0xFFFFu;
-                f.s[r][1] = sw >> 16;
-            } else {
-                const uint2 sw = *reinterpret_cast<const uint2*>(srow + chunk(0));
-                f.s[r][0] = sw.x & 0xFFFFu; f.s[r][1] = sw.x >> 16;
-                f.s[r][2] = sw.y & 0xFFFFu; f.s[r][3] = sw.y >> 16;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                f.q[r][j] = load_nt16(wrow + chunk(j) * 16);
-                f.s[r][j] = __builtin_nontemporal_load(srow + chunk(j));
-            }
+        for (int j = 0; j < NCH; ++j) {
+            f.q[r][j] = load_nt16(wrow + chunk(j) * 16);
+            f.s[r][j] = __builtin_nontemporal_load(srow + chunk(j));
         }
     };
 
@@ -304,15 +286,15 @@ constexpr int64_t kMaxLdsBytes = 64 * 1024;
 
 // Grid: about `blocks_per_cu` workgroups per CU on a 256-CU chip, never
 // more than there are row batches.
-template <int M, int NCH, int KS, int RW, bool CONTIG = false>
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads>
 hipError_t launch_cfg(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                       const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
                       int blocks_per_cu) {
-    constexpr int64_t groups = (kThreads / kWave) / KS;
+    constexpr int64_t groups = (THREADS / kWave) / KS;
     const int64_t nbatch = (N + RW - 1) / RW;
     int64_t grid = min((int64_t)256 * blocks_per_cu, (nbatch + groups - 1) / groups);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, CONTIG>), dim3((unsigned)grid), dim3(kThreads), 0, stream, x, N, K,
+    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, THREADS>), dim3((unsigned)grid), dim3(THREADS), 0, stream, x, N, K,
                        wc, ws, g0, g1, y);
     return hipGetLastError();
 }
@@ -332,16 +314,12 @@ template <int M>
 hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                     const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
     const bool fits_lds = (int64_t)M * K * 2 <= kMaxLdsBytes;
-    // measured on MI355X: one wave per 2048-wide row with four rows in
-    // flight for K = 2048; four waves splitting K with two rows in flight for
-    // K = 16384 (two workgroups per CU in both cases)
-    if (K == 2048) {
-        if constexpr (M <= 4) return launch_cfg<M, 1, 1, 4>(x, N, K, wc, ws, g0, g1, y, stream, 3);
-        else return launch_cfg<M, 1, 1, 2>(x, N, K, wc, ws, g0, g1, y, stream, 3);
-    }
-    if (K == 16384) {
-        if constexpr (M <= 4) return launch_cfg<M, 2, 4, 2>(x, N, K, wc, ws, g0, g1, y, stream, 2);
-    }
+    // measured on MI355X (o_proj 6144 x 16384 and q_b_proj 16384 x 2048):
+    // K = 2048: one wave per row, four rows in flight, three workgroups per
+    // CU (two for M > 4); K = 16384: eight waves split K (one 32-element
+    // chunk per lane), four rows in flight, one 512-thread workgroup per CU
+    if (K == 2048) return launch_cfg<M, 1, 1, 4>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2);
+    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512>(x, N, K, wc, ws, g0, g1, y, stream, 1);
     if (fits_lds) return launch_any<M, true>(x, N, K, wc, ws, g0, g1, y, stream);
     return launch_any<M, false>(x, N, K, wc, ws, g0, g1, y, stream);
 }

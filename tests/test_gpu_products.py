@@ -44,7 +44,7 @@ def test_gemv_tiny(orc, M):
     assert_close(host_bf16_f32(y), orc.gemv_w4a16(x, c0, s0, g0), f"gemv M={M}")
 
 
-@pytest.mark.parametrize("N,K", [(200, 2080), (1, 32), (67, 4096)])
+@pytest.mark.parametrize("N,K", [(200, 2080), (1, 32), (67, 4096), (37, 16384), (5, 2048)])
 def test_gemv_ragged(orc, N, K):
     w = wl.layer_weight((N, K), seed=N)
     x = wl.activations(2, K, seed=K)
@@ -55,7 +55,7 @@ def test_gemv_ragged(orc, N, K):
 
 
 @pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_layers_sampled(orc, name, M):
     w, x, (c0, s0, g0), (c, s, g) = _layer(name)
     xm = x[:M]
