@@ -252,6 +252,9 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
         return fail(NVFP4_ERR_WORKSPACE, "gemm: workspace smaller than nvfp4_gemm_w4a4_workspace_size%s");
     hipStream_t s = as_stream(stream);
     const GemmPlan p = plan_gemm(M, N, K);
+    if (p.gemv && gemv_quantizes_activation((int)M, K))
+        return hip_status(launch_gemv_w4a4(x, (int)M, N, K, w_codes, w_scales, w_global, input_scale, y, s),
+                          "gemm gemv");
     // Static activation quantization under input_scale.  The GEMM consumes the
     // quantized activation as the exact products q * s (f16 for the MFMA path,
     // bf16 for the GEMV), written directly by the quantizer; the two global

@@ -20,6 +20,7 @@
 //   * row sums are reduced across the wave with cross-lane shuffles.
 // Weights are read with non-temporal loads: each byte is used once.
 #include "nvfp4_device.hpp"
+#include "nvfp4_encode.hpp"
 #include "nvfp4_internal.hpp"
 
 #include <type_traits>
@@ -102,7 +103,12 @@ struct Frag {
 // refill is unconditional (no register copies).  Partial row sums are reduced
 // across the wave with shuffles and, when KS > 1, across the group's waves
 // through LDS.
-template <int M, int NCH, int KS, int RW, int THREADS = kThreads>
+//
+// With AQ (the W4A4 product at M = 1) x is the unquantized bf16 activation:
+// each lane NVFP4-encodes its slice under the static activation scale *g1
+// (the quantizer's block rule) and keeps the exact products q * s as bf16,
+// the operand the two-kernel path would read back from memory.
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false>
 __global__ __launch_bounds__(THREADS) void k_gemv(const uint16_t* __restrict__ x, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ wc,
                                                    const uint8_t* __restrict__ ws,
@@ -164,6 +170,20 @@ __global__ __launch_bounds__(THREADS) void k_gemv(const uint16_t* __restrict__ x
 #pragma unroll
             for (int i = 0; i < 4; ++i) xr[(m * NCH + j) * 4 + i] = p[i];
         }
+    if constexpr (AQ) {
+        const float sg = *g1, t = 6.0f * sg;
+#pragma unroll
+        for (int p = 0; p < M * NCH * 2; ++p) {
+            // 16-element block p: pieces 2p, 2p + 1 of the lane's slice
+            uint4& a = xr[2 * p];
+            uint4& b = xr[2 * p + 1];
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint2 codes;
+            const float sc = e4m3_to_f32(encode_block(w, sg, t, codes));
+            a = fp4x8_scaled_bf16_bits(codes.x, sc);
+            b = fp4x8_scaled_bf16_bits(codes.y, sc);
+        }
+    }
     const float scale = *g0 * (g1 ? *g1 : 1.0f);
 
     auto finish = [&](float (&acc)[RW][M], int64_t b, int it) {
@@ -286,7 +306,7 @@ constexpr int64_t kMaxLdsBytes = 64 * 1024;
 
 // Grid: about `blocks_per_cu` workgroups per CU on a 256-CU chip, never
 // more than there are row batches.
-template <int M, int NCH, int KS, int RW, int THREADS = kThreads>
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false>
 hipError_t launch_cfg(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                       const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
                       int blocks_per_cu) {
@@ -294,7 +314,7 @@ hipError_t launch_cfg(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc
     const int64_t nbatch = (N + RW - 1) / RW;
     int64_t grid = min((int64_t)256 * blocks_per_cu, (nbatch + groups - 1) / groups);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, THREADS>), dim3((unsigned)grid), dim3(THREADS), 0, stream, x, N, K,
+    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, THREADS, AQ>), dim3((unsigned)grid), dim3(THREADS), 0, stream, x, N, K,
                        wc, ws, g0, g1, y);
     return hipGetLastError();
 }
@@ -310,7 +330,7 @@ hipError_t launch_any(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc
     return hipGetLastError();
 }
 
-template <int M>
+template <int M, bool AQ = false>
 hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                     const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
     const bool fits_lds = (int64_t)M * K * 2 <= kMaxLdsBytes;
@@ -318,17 +338,17 @@ hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, 
     // K = 2048: one wave per row, four rows in flight, three workgroups per
     // CU (two for M > 4); K = 16384: eight waves split K (one 32-element
     // chunk per lane), four rows in flight, one 512-thread workgroup per CU
-    if (K == 2048) return launch_cfg<M, 1, 1, 4>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2);
-    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512>(x, N, K, wc, ws, g0, g1, y, stream, 1);
+    if (K == 2048)
+        return launch_cfg<M, 1, 1, 4, kThreads, AQ>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2);
+    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512, AQ>(x, N, K, wc, ws, g0, g1, y, stream, 1);
+    if constexpr (AQ) return hipErrorNotSupported;
     if (fits_lds) return launch_any<M, true>(x, N, K, wc, ws, g0, g1, y, stream);
     return launch_any<M, false>(x, N, K, wc, ws, g0, g1, y, stream);
 }
 
-}  // namespace
-
-hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
-                             const uint8_t* ws, const float* g0, const float* g1, uint16_t* y,
-                             hipStream_t stream) {
+hipError_t launch_batch(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
+                        const uint8_t* ws, const float* g0, const float* g1, uint16_t* y,
+                        hipStream_t stream) {
     switch (M) {
         case 1: return launch_m<1>(x, N, K, wc, ws, g0, g1, y, stream);
         case 2: return launch_m<2>(x, N, K, wc, ws, g0, g1, y, stream);
@@ -340,6 +360,27 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, con
         case 8: return launch_m<8>(x, N, K, wc, ws, g0, g1, y, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
+                             const uint8_t* ws, const float* g0, const float* g1, uint16_t* y,
+                             hipStream_t stream) {
+    return launch_batch(x, M, N, K, wc, ws, g0, g1, y, stream);
+}
+
+// Measured on MI355X: the in-register quantize costs each lane 2 M block
+// encodes up front; at M = 1 that hides behind the first weight loads and
+// saves the separate quantize launch, from M = 2 on the two-kernel path is
+// as fast or faster.
+bool gemv_quantizes_activation(int M, int64_t K) { return M == 1 && (K == 2048 || K == 16384); }
+
+hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
+                            const uint8_t* ws, const float* w_global, const float* input_scale,
+                            uint16_t* y, hipStream_t stream) {
+    if (!gemv_quantizes_activation(M, K)) return hipErrorNotSupported;
+    return launch_m<1, true>(x, N, K, wc, ws, w_global, input_scale, y, stream);
 }
 
 }  // namespace nvfp4

@@ -60,6 +60,16 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, con
                              const uint8_t* ws, const float* g0, const float* g1, uint16_t* y,
                              hipStream_t stream);
 
+// W4A4 at M = 1 in one launch: the GEMV quantizes the bf16 activation x
+// under *input_scale in registers (same codes and scales as
+// launch_quantize_pack in static mode) and multiplies with the exact q * s;
+// y = bf16(*w_global * *input_scale * sum).  Available when
+// gemv_quantizes_activation(M, K); hipErrorNotSupported otherwise.
+bool gemv_quantizes_activation(int M, int64_t K);
+hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
+                            const uint8_t* ws, const float* w_global, const float* input_scale,
+                            uint16_t* y, hipStream_t stream);
+
 // -------------------------------------------------------------------- GEMM --
 
 // A operand formats: bf16 values, or f16 values that are the exact products

@@ -106,6 +106,56 @@ def test_gemm_layers_sampled(orc, name, M):
     assert_close(y[np.ix_(rows, cols)], ref, f"gemm {name} M={M}")
 
 
+def _two_step_small_m(orc, x, isc, c, s, g):
+    """The small-M W4A4 product written as two library calls: static quantize,
+    then the W4A16 GEMV over the exact products q * s (bf16) under the
+    combined global scale fl(w_global * input_scale)."""
+    xc, xs, _ = nv.quantize(dev_bf16(x), static_scale=float(isc))
+    torch.cuda.synchronize()
+    _, qs = orc.dequantize(host_u8(xc), host_u8(xs), 1.0, want_bf16=True)
+    gcomb = torch.tensor([np.float32(g.cpu().item()) * np.float32(isc)], device=device())
+    y = nv.gemv_w4a16(dev_bf16(qs), c, s, gcomb)
+    torch.cuda.synchronize()
+    return host_bf16_f32(y)
+
+
+@pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemm_small_m_equals_two_step(orc, name, M):
+    # At M = 1 on these shapes the GEMM quantizes the activation inside the
+    # GEMV (other small M run the two kernels); either way the result must be
+    # bit-identical to quantizing first.
+    w, _, _, (c, s, g) = _layer(name)
+    x = wl.activations(M, w.shape[1], seed=90 + M)
+    isc = np.float32(orc.global_scale(x))
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    np.testing.assert_array_equal(y.view(np.uint32), _two_step_small_m(orc, x, isc, c, s, g).view(np.uint32))
+
+
+@pytest.mark.parametrize("f", [0.02, 1.0, 64.0])
+@pytest.mark.parametrize("K", [2048, 16384])
+def test_gemm_batch1_edge_blocks(orc, f, K):
+    # single rows with zero blocks, outlier blocks, tiny values and an input
+    # scale far too small (saturated block scales) or too large (subnormal
+    # block scales) for the activation
+    N = 96
+    w = wl.layer_weight((N, K), seed=12)
+    x = wl.bf16_bits_to_f32(wl.activations(4, K, seed=13)).copy()
+    x[0, :64] = 0.0
+    x[1, 32:48] *= 3000.0
+    x[2, ::17] = -1e-30
+    x[3] *= 1e-6
+    x = wl.to_bf16_bits(x)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    for r in range(4):
+        xr = x[r:r + 1]
+        isc = np.float32(orc.global_scale(xr) * f)
+        y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(xr), torch.tensor([isc], device=device()), c, s, g))
+        np.testing.assert_array_equal(y.view(np.uint32),
+                                      _two_step_small_m(orc, xr, isc, c, s, g).view(np.uint32))
+        assert_close(y, orc.gemm_w4a4(xr, isc, c0, s0, g0), f"gemm row {r} K={K} x{f}")
+
+
 def test_gemm_generous_and_tight_input_scale(orc):
     w = wl.layer_weight((256, 1024), seed=5)
     x = wl.activations(160, 1024, seed=6)
