@@ -132,33 +132,42 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
     }
 }
 
-// Dequantize: one 16-element block per thread per iteration.
-__global__ __launch_bounds__(kThreads) void k_dequantize(const uint2* __restrict__ codes,
+// Dequantize: one piece of 8 elements (4 code bytes, half a block) per
+// thread per step, two steps per iteration with both loads issued first.
+// Consecutive threads take consecutive pieces, so every load and every
+// 16-byte store of a wave is contiguous; non-temporal both ways (each byte is
+// touched once).
+__device__ __forceinline__ u32x4 dequant_piece(uint32_t c, uint32_t sbyte, float Sg) {
+    const float s = e4m3_to_f32(sbyte);
+    f32x2 q[4];
+    fp4x8_to_f32(c, q);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float qs0 = q[i].x * s, qs1 = q[i].y * s;
+        const float v0 = qs0 * Sg, v1 = qs1 * Sg;
+        o[i] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          const float* __restrict__ sg_ptr,
-                                                         float sg_const, int64_t nblk,
-                                                         uint4* __restrict__ y) {
+                                                         float sg_const, int64_t npiece,
+                                                         u32x4* __restrict__ y) {
     const float Sg = sg_ptr ? *sg_ptr : sg_const;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-        const uint2 c = codes[b];
-        const float s = e4m3_to_f32(scales[b]);
-        uint32_t out[8];
-        const uint32_t cw[2] = {c.x, c.y};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x2 q[4];
-            fp4x8_to_f32(cw[h], q);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float qs0 = q[i].x * s, qs1 = q[i].y * s;
-                float v0 = qs0 * Sg, v1 = qs1 * Sg;
-                out[h * 4 + i] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
-            }
-        }
-        y[2 * b] = make_uint4(out[0], out[1], out[2], out[3]);
-        y[2 * b + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+    int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; p + stride < npiece; p += 2 * stride) {
+        const uint32_t c0 = __builtin_nontemporal_load(codes + p);
+        const uint32_t c1 = __builtin_nontemporal_load(codes + p + stride);
+        const uint32_t s0 = __builtin_nontemporal_load(scales + (p >> 1));
+        const uint32_t s1 = __builtin_nontemporal_load(scales + ((p + stride) >> 1));
+        __builtin_nontemporal_store(dequant_piece(c0, s0, Sg), y + p);
+        __builtin_nontemporal_store(dequant_piece(c1, s1, Sg), y + p + stride);
     }
+    if (p < npiece) __builtin_nontemporal_store(dequant_piece(codes[p], scales[p >> 1], Sg), y + p);
 }
 
 int grid_for(int64_t work, int per_block, int cap) {
@@ -202,11 +211,13 @@ hipError_t launch_quantize_pack(const PackArgs& a, hipStream_t stream) {
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* sg_ptr,
                              float sg_const, int64_t rows, int64_t cols, uint16_t* y,
                              hipStream_t stream) {
-    const int64_t nblk = rows * (cols / 16);
-    const int grid = grid_for(nblk, kThreads, 8192);
+    // about three pieces per thread (measured on MI355X: the store stream
+    // wants tens of thousands of workgroups)
+    const int64_t npiece = rows * (cols / 8);
+    const int grid = grid_for(npiece, kThreads * 3, 65536);
     hipLaunchKernelGGL(k_dequantize, dim3(grid), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint2*>(codes), scales, sg_ptr, sg_const, nblk,
-                       reinterpret_cast<uint4*>(y));
+                       reinterpret_cast<const uint32_t*>(codes), scales, sg_ptr, sg_const, npiece,
+                       reinterpret_cast<u32x4*>(y));
     return hipGetLastError();
 }
 
