@@ -105,8 +105,11 @@ struct Cfg {
     static_assert(2 * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
+// WPE: minimum waves per SIMD the register allocation must allow (1: no
+// constraint beyond the workgroup size).
+template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP, int WPE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE)))
+void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN>;
     using Op = typename OpOf<AF>::T;
     constexpr int BM = C::BM, BN = C::BN, WTM = C::WTM, WTN = C::WTN;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_a16(GemmArgs g) {
     }
 }
 
-template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP>
+template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP, int WPE = 1>
 hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     using C = Cfg<TM, TN, WM, WN>;
     GemmArgs g = g0;
@@ -397,19 +400,19 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     } else {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, PD, AF, EP>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, PD, AF, EP, WPE>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
 }
 
 template <AFmt AF, Epi EP>
 hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t stream) {
     switch (tile) {
-        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
         case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, 1, AF, EP>(g, grid_m, stream);
         case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 1, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP, 3>(g, grid_m, stream);
         case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
         case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
