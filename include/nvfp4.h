@@ -134,6 +134,24 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * W4A16 GEMM over any M: the weight-only path of the model card
+ * "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "Kernel choice", measured against
+ * W4A4 across the batch sweep (that section compares the two kernel families
+ * from batch 1 upward).  Same product as the GEMV,
+ * y[m, n] = bf16( Sg_w * sum_k s[n, k/16] * q[n, k] * x[m, k] ), fp32
+ * accumulation, with x bf16 [M, K] used as is (no activation quantization).
+ * Small M runs the GEMV kernels; larger M runs MFMA tiles whose weight
+ * operand is decoded to the exact bf16 values q * s.  K % 64 == 0, and when
+ * the tiles run the weight codes must span less than 2 GiB; else UNSUPPORTED.
+ * Workspace: nvfp4_gemm_w4a16_workspace_size(M, N, K) bytes (split-K partial
+ * sums; 0 when none are needed, and then workspace may be NULL).
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K);
+int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_global, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Routed-expert MoE layer with NVFP4 experts ("GLM-5.2-NVFP4" model card:
  * 256 routed experts, 8 per token, hidden 6144, experts quantized to NVFP4;
  * W4A4 variant as in "vroomfondel/glm-5.2-reap-504B-v2-W4A4").

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "nvfp4_gemv_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P]),
             "nvfp4_gemm_w4a4_workspace_size": (SZ, [I64, I64, I64]),
             "nvfp4_gemm_w4a4": (I32, [P, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
+            "nvfp4_gemm_w4a16_workspace_size": (SZ, [I64, I64, I64]),
+            "nvfp4_gemm_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P, SZ, P]),
             "nvfp4_moe_workspace_size": (SZ, [ctypes.POINTER(MoeProblem)]),
             "nvfp4_moe_grouped_gemm": (I32, [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors),
                                              P, SZ, P]),
@@ -130,6 +132,10 @@ def gemm_w4a4_workspace_size(M: int, N: int, K: int) -> int:
     return int(lib().nvfp4_gemm_w4a4_workspace_size(M, N, K))
 
 
+def gemm_w4a16_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_w4a16_workspace_size(M, N, K))
+
+
 def moe_workspace_size(T, E, top_k, H, I, mode) -> int:
     p = MoeProblem(T, E, top_k, H, I, mode)
     return int(lib().nvfp4_moe_workspace_size(ctypes.byref(p)))
@@ -189,6 +195,20 @@ def gemm_w4a4(x, input_scale, w_codes, w_scales, w_global, out=None, ws=None, st
     _check(lib().nvfp4_gemm_w4a4(_ptr(x), _ptr(isc), M, N, K, _ptr(w_codes), _ptr(w_scales),
                                  _ptr(w_global), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "nvfp4_gemm_w4a4")
+    return out
+
+
+def gemm_w4a16(x, w_codes, w_scales, w_global, out=None, ws=None, stream=None):
+    x = _bf16(x)
+    M, K = x.shape
+    N = w_codes.shape[0]
+    dev = x.device
+    out = _empty((M, N), torch.bfloat16, dev) if out is None else out
+    if ws is None:
+        ws = workspace(gemm_w4a16_workspace_size(M, N, K), dev)
+    _check(lib().nvfp4_gemm_w4a16(_ptr(x), M, N, K, _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "nvfp4_gemm_w4a16")
     return out
 
 

@@ -88,6 +88,53 @@ GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
     return l;
 }
 
+// W4A16 GEMM workspace: split-K partial sums only (the activation is the
+// bf16 operand itself).
+GemmLayout layout_gemm_w4a16(int64_t M, int64_t N, int64_t K) {
+    GemmLayout l;
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (!p.gemv && p.ksplit > 1) l.total = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
+    l.partial = 0;
+    return l;
+}
+
+// The MFMA-tile path shared by both GEMMs: A is a 16-bit [M, K] operand (f16
+// q * s for W4A4, the bf16 activation for W4A16), in launches of at most
+// gemm_chunk_rows rows; split K reduces through `partial`.
+hipError_t run_gemm_tiles(const GemmPlan& p, const uint16_t* a, AFmt afmt, const float* a_global, int64_t M,
+                          int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const float* w_global, uint16_t* y, float* partial, hipStream_t s) {
+    const int64_t chunk = gemm_chunk_rows(M, K);
+    for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+        const int64_t rows = (M - r0 < chunk) ? M - r0 : chunk;
+        GemmArgs g;
+        g.a = a + r0 * K;
+        g.a_src_rows = rows;
+        g.a_global = a_global;
+        g.b_codes = w_codes;
+        g.b_scales = w_scales;
+        g.b_global = w_global;
+        g.M = rows;
+        g.N = N;
+        g.K = K;
+        g.ksplit = p.ksplit;
+        hipError_t e;
+        if (p.ksplit > 1) {
+            g.out = partial;
+            g.ldo = N;
+            e = launch_gemm_a16(g, afmt, Epi::kPartialF32, p.tile, 0, s);
+            if (e != hipSuccess) return e;
+            e = launch_splitk_reduce(partial, p.ksplit, rows, N, w_global, a_global, y + r0 * N, s);
+        } else {
+            g.out = y + r0 * N;
+            g.ldo = N;
+            e = launch_gemm_a16(g, afmt, Epi::kStoreBf16, p.tile, 0, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // ------------------------------------------------------------ MoE planning --
 
 // Row tile of the grouped GEMMs (a group's rows are covered by tiles of this
@@ -273,36 +320,42 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (p.gemv)
         return hip_status(launch_gemv_w4a16(xh, (int)M, N, K, w_codes, w_scales, w_global, input_scale, y, s),
                           "gemm gemv");
-    const int64_t chunk = gemm_chunk_rows(M, K);
-    for (int64_t r0 = 0; r0 < M; r0 += chunk) {
-        const int64_t rows = (M - r0 < chunk) ? M - r0 : chunk;
-        GemmArgs g;
-        g.a = xh + r0 * K;
-        g.a_src_rows = rows;
-        g.a_global = input_scale;
-        g.b_codes = w_codes;
-        g.b_scales = w_scales;
-        g.b_global = w_global;
-        g.M = rows;
-        g.N = N;
-        g.K = K;
-        g.ksplit = p.ksplit;
-        if (p.ksplit > 1) {
-            float* part = at<float>(workspace, l.partial);
-            g.out = part;
-            g.ldo = N;
-            st = hip_status(launch_gemm_a16(g, AFmt::kF16, Epi::kPartialF32, p.tile, 0, s), "gemm");
-            if (st) return st;
-            st = hip_status(launch_splitk_reduce(part, p.ksplit, rows, N, input_scale, w_global, y + r0 * N, s),
-                            "gemm split-k reduce");
-        } else {
-            g.out = y + r0 * N;
-            g.ldo = N;
-            st = hip_status(launch_gemm_a16(g, AFmt::kF16, Epi::kStoreBf16, p.tile, 0, s), "gemm");
-        }
-        if (st) return st;
-    }
-    return NVFP4_OK;
+    return hip_status(run_gemm_tiles(p, xh, AFmt::kF16, input_scale, M, N, K, w_codes, w_scales, w_global, y,
+                                     p.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                      "gemm");
+}
+
+size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
+    return layout_gemm_w4a16(M, N, K).total;
+}
+
+int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_global, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "gemm_w4a16: need M, N >= 0, K > 0 and K %% 16 == 0%s");
+    if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm_w4a16: K must be a multiple of 64%s");
+    if (!plan_gemm(M, N, K).gemv && ((int64_t)N * (K / 2) >= kMaxOperandBytes || gemm_chunk_rows(M, K) < 1))
+        return fail(NVFP4_ERR_UNSUPPORTED, "gemm_w4a16: weight matrix of 2 GiB or more%s");
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!x || !w_codes || !w_scales || !w_global || !y)
+        return fail(NVFP4_ERR_NULL_ARG, "gemm_w4a16: x, weights and y are required%s");
+    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned4(w_global) || !aligned16(y) ||
+        (workspace && !aligned16(workspace)))
+        return fail(NVFP4_ERR_ALIGN, "gemm_w4a16: pointers must be 16-byte aligned%s");
+    const GemmLayout l = layout_gemm_w4a16(M, N, K);
+    if (l.total > 0 && (!workspace || workspace_bytes < l.total))
+        return fail(NVFP4_ERR_WORKSPACE, "gemm_w4a16: workspace smaller than nvfp4_gemm_w4a16_workspace_size%s");
+    hipStream_t s = as_stream(stream);
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (p.gemv)
+        return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y, s),
+                          "gemm_w4a16 gemv");
+    return hip_status(run_gemm_tiles(p, x, AFmt::kBf16, nullptr, M, N, K, w_codes, w_scales, w_global, y,
+                                     p.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                      "gemm_w4a16");
 }
 
 // --------------------------------------------------------------------- MoE --

@@ -20,7 +20,7 @@ MIS = 4097        # misaligned
 def test_exports_every_header_symbol():
     L = ctypes.CDLL(nv.LIB_PATH)
     names = nv.header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
 
@@ -81,6 +81,22 @@ def test_gemm_validation():
     assert g(A, A, 128, 256, 512, A, A, A, A, None, 0, None) == WS
     assert g(A, A, 128, 256, 512, A, A, A, A, MIS, ws, None) == ALIGN
     assert g(A, A, 0, 256, 512, A, A, A, A, None, 0, None) == OK
+
+
+def test_gemm_w4a16_validation():
+    L = nv.lib()
+    g = L.nvfp4_gemm_w4a16
+    ws = L.nvfp4_gemm_w4a16_workspace_size(128, 256, 4096)
+    assert ws > 0                                            # split K: partial sums
+    assert L.nvfp4_gemm_w4a16_workspace_size(4096, 6144, 16384) == 0
+    assert g(None, 128, 256, 4096, A, A, A, A, A, ws, None) == NULL
+    assert g(A, 128, 256, 4100, A, A, A, A, A, ws, None) == SHAPE
+    assert g(A, 128, 256, 4128, A, A, A, A, A, 1 << 30, None) == UNSUP   # K % 64 != 0
+    assert g(A, 128, 256, 4096, A, A, A, A, A, ws - 1, None) == WS
+    assert g(A, 128, 256, 4096, A, A, A, A, None, 0, None) == WS
+    assert g(A, 128, 256, 4096, A, A, A, MIS, A, ws, None) == ALIGN
+    assert g(A, 0, 256, 4096, A, A, A, A, None, 0, None) == OK
+    assert g(A, 5, 0, 4096, A, A, A, A, None, 0, None) == OK
 
 
 def test_moe_validation():

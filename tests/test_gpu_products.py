@@ -106,6 +106,41 @@ def test_gemm_layers_sampled(orc, name, M):
     assert_close(y[np.ix_(rows, cols)], ref, f"gemm {name} M={M}")
 
 
+# ------------------------------------------------------- W4A16 over any M --
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (6, 200, 8192), (9, 200, 256), (37, 200, 256),
+                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640)])
+def test_gemm_w4a16_shapes(orc, M, N, K):
+    w = wl.layer_weight((N, K), seed=M * 5 + N)
+    x = wl.activations(M, K, seed=M + K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    y = nv.gemm_w4a16(dev_bf16(x), c, s, g)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), orc.gemv_w4a16(x, c0, s0, g0), f"gemm_w4a16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
+@pytest.mark.parametrize("M", list(wl.GEMM_M_SWEEP))
+def test_gemm_w4a16_layers_sampled(orc, name, M):
+    w, _, (c0, s0, g0), (c, s, g) = _layer(name)
+    x = wl.activations(M, w.shape[1], seed=4)
+    y = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    rng = np.random.default_rng(M + 1)
+    rows = np.sort(rng.choice(M, min(M, 48), replace=False))
+    cols = np.sort(rng.choice(w.shape[0], 96, replace=False))
+    ref = orc.gemv_w4a16(x[rows], c0[cols], s0[cols], g0)
+    assert_close(y[np.ix_(rows, cols)], ref, f"gemm_w4a16 {name} M={M}")
+
+
+def test_gemm_w4a16_small_m_equals_gemv(orc):
+    # at M <= 8 the GEMM entry point runs the GEMV kernels: same bits
+    w, _, _, (c, s, g) = _layer("o_proj")
+    x = wl.activations(4, w.shape[1], seed=8)
+    a = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    b = host_bf16_f32(nv.gemv_w4a16(dev_bf16(x), c, s, g))
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def _two_step_small_m(orc, x, isc, c, s, g):
     """The small-M W4A4 product written as two library calls: static quantize,
     then the W4A16 GEMV over the exact products q * s (bf16) under the
