@@ -3,8 +3,8 @@
 One step = one pass over every kernel of the path on its full-size synthetic
 workload: dynamic quantize and dequantize of a 65536 x 6144 heavy-tailed bf16
 tensor; the W4A16 GEMV at batch 1, 2, 4, 8 on o_proj (6144 x 16384) and
-q_b_proj (16384 x 2048); the W4A4 and the W4A16 GEMM at M in {1, 8, ...,
-4096} on both shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
+q_b_proj (16384 x 2048); the W4A4 GEMM (from bf16 and from a pre-packed
+activation) and the W4A16 GEMM at M in {1, 8, ..., 4096} on both shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
 6144, intermediate 2048) in W4A16 and W4A4 mode.  Inputs are resident in HBM
 before timing starts.  Weight-streaming kernels cycle through enough weight
 copies that every launch reads its weights from HBM, not from the 256 MB
@@ -308,6 +308,19 @@ def main():
                 rows.append(Row(f"gemm_w4a4_{name}_M{M}", calls, reps, nbytes=wbytes + 2 * M * K + 2 * M * N,
                                 keep=(x, isc, y, ws, use),
                                 flops=2.0 * M * N * K, info={"M": M, "N": N, "K": K}))
+                # the same product on the activation pre-packed by a static quantize (serving split)
+                ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+                asc = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+                ag = torch.empty(4, dtype=torch.float32, device=dev)
+                check(L.nvfp4_quantize(P(x), M, K, P(isc), P(ac), P(asc), P(ag), None, 0, sptr), "static quantize")
+                wsp = nv.workspace(L.nvfp4_gemm_w4a4_packed_workspace_size(M, N, K), dev)
+                callsp = []
+                for c, s, g in use:
+                    a = (P(ac), P(asc), P(ag), M, N, K, P(c), P(s), P(g), P(y), P(wsp), wsp.numel(), sptr)
+                    callsp.append(lambda a=a: check(L.nvfp4_gemm_w4a4_packed(*a), "gemm_packed"))
+                rows.append(Row(f"gemm_w4a4_packed_{name}_M{M}", callsp, reps,
+                                nbytes=wbytes + M * K * (0.5 + 1 / 16) + 2 * M * N, keep=(ac, asc, ag, y, wsp, use),
+                                flops=2.0 * M * N * K, info={"M": M, "N": N, "K": K}))
                 # the weight-only path on the same activation (bf16 operand, no quantize)
                 ws16 = nv.workspace(nv.gemm_w4a16_workspace_size(M, N, K), dev)
                 calls16 = []
@@ -435,7 +448,7 @@ def main():
         "data": "synthetic (seeded numpy draws, bf16; NVFP4 weights quantized on the GPU)",
         "config": {"workload": "W4A16 batch-1 decode GEMV on NVFP4 o_proj [6144 x 16384]; step also runs "
                                "quantize/dequantize 65536x6144, GEMV M=1..8 on o_proj and q_b_proj, "
-                               "W4A4 and W4A16 GEMM M=1..4096 on both, MoE T=4096 E=256 top-8 H=6144 I=2048",
+                               "W4A4 (bf16 and pre-packed activation) and W4A16 GEMM M=1..4096 on both, MoE T=4096 E=256 top-8 H=6144 I=2048",
                    "gpu": torch.cuda.get_device_name(0), "setup_s": round(setup_s, 1),
                    "timing": "HIP events around back-to-back launches enqueued behind a prefill kernel"},
         "roofline": roofline, "cpu_baseline": cpu, "rows": report,

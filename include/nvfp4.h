@@ -134,6 +134,26 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * W4A4 GEMM on a pre-packed NVFP4 activation: the serving split in which a
+ * producer quantizes X once under the static input_scale (nvfp4_quantize in
+ * static mode; model card "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "How it
+ * was produced": static input_scale, no dynamic activation quantization) and
+ * the GEMM consumes codes and scales.
+ * y[m, n] = bf16( a_global * Sg_w * sum_b sx[m,b] sw[n,b] sum_{k in b} qx qw ),
+ * fp32 accumulation; identical to nvfp4_gemm_w4a4 on the X those codes came
+ * from.  a_codes [M, K/2], a_scales [M, K/16], a_global device fp32 [1] (the
+ * static scale the codes were made with); w_* as in the GEMV; y bf16 [M, N].
+ * Same shape limits as nvfp4_gemm_w4a4.  Workspace:
+ * nvfp4_gemm_w4a4_packed_workspace_size(M, N, K) bytes (the activation
+ * expanded to its exact products q * s, and split-K partial sums).
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_gemm_w4a4_packed_workspace_size(int64_t M, int64_t N, int64_t K);
+int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t M,
+                               int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* w_global, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * W4A16 GEMM over any M: the weight-only path of the model card
  * "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "Kernel choice", measured against
  * W4A4 across the batch sweep (that section compares the two kernel families

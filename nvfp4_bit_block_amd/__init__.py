@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "nvfp4_gemv_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P]),
             "nvfp4_gemm_w4a4_workspace_size": (SZ, [I64, I64, I64]),
             "nvfp4_gemm_w4a4": (I32, [P, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
+            "nvfp4_gemm_w4a4_packed_workspace_size": (SZ, [I64, I64, I64]),
+            "nvfp4_gemm_w4a4_packed": (I32, [P, P, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
             "nvfp4_gemm_w4a16_workspace_size": (SZ, [I64, I64, I64]),
             "nvfp4_gemm_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P, SZ, P]),
             "nvfp4_moe_workspace_size": (SZ, [ctypes.POINTER(MoeProblem)]),
@@ -195,6 +197,22 @@ def gemm_w4a4(x, input_scale, w_codes, w_scales, w_global, out=None, ws=None, st
     _check(lib().nvfp4_gemm_w4a4(_ptr(x), _ptr(isc), M, N, K, _ptr(w_codes), _ptr(w_scales),
                                  _ptr(w_global), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "nvfp4_gemm_w4a4")
+    return out
+
+
+def gemm_w4a4_packed(a_codes, a_scales, a_global, w_codes, w_scales, w_global, out=None, ws=None,
+                     stream=None):
+    M, half = a_codes.shape
+    K = half * 2
+    N = w_codes.shape[0]
+    dev = a_codes.device
+    out = _empty((M, N), torch.bfloat16, dev) if out is None else out
+    if ws is None:
+        ws = workspace(int(lib().nvfp4_gemm_w4a4_packed_workspace_size(M, N, K)), dev)
+    _check(lib().nvfp4_gemm_w4a4_packed(_ptr(a_codes), _ptr(a_scales), _ptr(a_global), M, N, K, _ptr(w_codes),
+                                        _ptr(w_scales), _ptr(w_global), _ptr(out), _ptr(ws), ws.numel(),
+                                        _stream(stream)),
+           "nvfp4_gemm_w4a4_packed")
     return out
 
 

@@ -325,6 +325,45 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
                       "gemm");
 }
 
+size_t nvfp4_gemm_w4a4_packed_workspace_size(int64_t M, int64_t N, int64_t K) {
+    return nvfp4_gemm_w4a4_workspace_size(M, N, K);
+}
+
+int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t M,
+                               int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* w_global, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    g_last_error[0] = '\0';
+    if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "gemm_packed: need M, N >= 0, K > 0 and K %% 16 == 0%s");
+    if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm_packed: K must be a multiple of 64%s");
+    if (!plan_gemm(M, N, K).gemv && ((int64_t)N * (K / 2) >= kMaxOperandBytes || gemm_chunk_rows(M, K) < 1))
+        return fail(NVFP4_ERR_UNSUPPORTED, "gemm_packed: weight matrix of 2 GiB or more%s");
+    if (M == 0 || N == 0) return NVFP4_OK;
+    if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !y)
+        return fail(NVFP4_ERR_NULL_ARG, "gemm_packed: activation, weights and y are required%s");
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned4(a_global) || !aligned16(w_codes) ||
+        !aligned16(w_scales) || !aligned4(w_global) || !aligned16(y) || (workspace && !aligned16(workspace)))
+        return fail(NVFP4_ERR_ALIGN, "gemm_packed: pointers must be 16-byte aligned%s");
+    const GemmLayout l = layout_gemm(M, N, K);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(NVFP4_ERR_WORKSPACE, "gemm_packed: workspace smaller than nvfp4_gemm_w4a4_packed_workspace_size%s");
+    hipStream_t s = as_stream(stream);
+    const GemmPlan p = plan_gemm(M, N, K);
+    // The packed activation is expanded to its exact products q * s, the
+    // operand form of both kernels (bf16 for the GEMV, f16 for the tiles);
+    // the two global scales are applied after the contraction.
+    uint16_t* xh = at<uint16_t>(workspace, l.xhat);
+    int32_t st = hip_status(launch_expand_qs(a_codes, a_scales, M, K, xh, p.gemv, s), "gemm_packed expand");
+    if (st) return st;
+    if (p.gemv)
+        return hip_status(launch_gemv_w4a16(xh, (int)M, N, K, w_codes, w_scales, w_global, a_global, y, s),
+                          "gemm_packed gemv");
+    return hip_status(run_gemm_tiles(p, xh, AFmt::kF16, a_global, M, N, K, w_codes, w_scales, w_global, y,
+                                     p.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                      "gemm_packed");
+}
+
 size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
     return layout_gemm_w4a16(M, N, K).total;

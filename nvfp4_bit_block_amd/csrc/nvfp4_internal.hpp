@@ -53,6 +53,11 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                              float sg_const, int64_t rows, int64_t cols, uint16_t* y,
                              hipStream_t stream);
 
+// Packed codes + scales [rows, cols] -> the exact products q * s (no global
+// scale), f16 or bf16 [rows, cols].
+hipError_t launch_expand_qs(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                            uint16_t* out, bool bf16, hipStream_t stream);
+
 // -------------------------------------------------------------------- GEMV --
 
 // y[m, n] = bf16(scale * sum_k s*q*x), scale = *g0 * (g1 ? *g1 : 1).

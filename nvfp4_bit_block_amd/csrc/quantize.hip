@@ -170,6 +170,22 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t* __restr
     if (p < npiece) __builtin_nontemporal_store(dequant_piece(codes[p], scales[p >> 1], Sg), y + p);
 }
 
+// Packed NVFP4 -> the exact products q * s (no global scale) as f16 or bf16,
+// one 8-element piece per thread per step: the operand form the GEMM and
+// GEMV kernels consume.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_expand_qs(const uint32_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        int64_t npiece, uint4* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x; p < npiece; p += stride) {
+        const uint32_t c = __builtin_nontemporal_load(codes + p);
+        const float s = e4m3_to_f32(__builtin_nontemporal_load(scales + (p >> 1)));
+        if constexpr (BF16) out[p] = fp4x8_scaled_bf16_bits(c, s);
+        else out[p] = __builtin_bit_cast(uint4, fp4x8_scaled_f16(c, (_Float16)s));
+    }
+}
+
 int grid_for(int64_t work, int per_block, int cap) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;
@@ -218,6 +234,17 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
     hipLaunchKernelGGL(k_dequantize, dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint32_t*>(codes), scales, sg_ptr, sg_const, npiece,
                        reinterpret_cast<u32x4*>(y));
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_qs(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                            uint16_t* out, bool bf16, hipStream_t stream) {
+    const int64_t npiece = rows * (cols / 8);
+    const int grid = grid_for(npiece, kThreads * 3, 65536);
+    const uint32_t* c = reinterpret_cast<const uint32_t*>(codes);
+    uint4* o = reinterpret_cast<uint4*>(out);
+    if (bf16) hipLaunchKernelGGL(k_expand_qs<true>, dim3(grid), dim3(kThreads), 0, stream, c, scales, npiece, o);
+    else hipLaunchKernelGGL(k_expand_qs<false>, dim3(grid), dim3(kThreads), 0, stream, c, scales, npiece, o);
     return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ MIS = 4097        # misaligned
 def test_exports_every_header_symbol():
     L = ctypes.CDLL(nv.LIB_PATH)
     names = nv.header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
 
@@ -81,6 +81,20 @@ def test_gemm_validation():
     assert g(A, A, 128, 256, 512, A, A, A, A, None, 0, None) == WS
     assert g(A, A, 128, 256, 512, A, A, A, A, MIS, ws, None) == ALIGN
     assert g(A, A, 0, 256, 512, A, A, A, A, None, 0, None) == OK
+
+
+def test_gemm_packed_validation():
+    L = nv.lib()
+    g = L.nvfp4_gemm_w4a4_packed
+    ws = L.nvfp4_gemm_w4a4_packed_workspace_size(128, 256, 512)
+    assert ws == L.nvfp4_gemm_w4a4_workspace_size(128, 256, 512) > 0
+    assert g(A, A, None, 128, 256, 512, A, A, A, A, A, ws, None) == NULL
+    assert g(A, A, A, 128, 256, 520, A, A, A, A, A, ws, None) == SHAPE
+    assert g(A, A, A, 128, 256, 528, A, A, A, A, A, 1 << 30, None) == UNSUP   # K % 64 != 0
+    assert g(A, A, A, 128, 256, 512, A, A, A, A, A, ws - 1, None) == WS
+    assert g(A, A, A, 128, 256, 512, A, A, A, A, None, 0, None) == WS
+    assert g(A, MIS, A, 128, 256, 512, A, A, A, A, A, ws, None) == ALIGN
+    assert g(A, A, A, 0, 256, 512, A, A, A, A, None, 0, None) == OK
 
 
 def test_gemm_w4a16_validation():

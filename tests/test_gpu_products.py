@@ -106,6 +106,37 @@ def test_gemm_layers_sampled(orc, name, M):
     assert_close(y[np.ix_(rows, cols)], ref, f"gemm {name} M={M}")
 
 
+# ------------------------------------------- W4A4 on a pre-packed activation --
+
+def _packed_matches(orc, x, isc, c, s, g, what):
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    ac, asc, ag = nv.quantize(dev_bf16(x), static_scale=float(isc))
+    yp = host_bf16_f32(nv.gemm_w4a4_packed(ac, asc, ag, c, s, g))
+    np.testing.assert_array_equal(yp.view(np.uint32), y.view(np.uint32), err_msg=what)
+    return yp
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (3, 200, 2048), (9, 200, 256), (37, 200, 256),
+                                   (130, 384, 512), (300, 136, 640)])
+def test_gemm_packed_shapes(orc, M, N, K):
+    # quantize once (static), then the GEMM on codes and scales: the same bits
+    # as the one-call W4A4 GEMM, and within tolerance of the oracle
+    w = wl.layer_weight((N, K), seed=M * 3 + N)
+    x = wl.activations(M, K, seed=M + 2 * K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))
+    yp = _packed_matches(orc, x, isc, c, s, g, f"packed {M}x{N}x{K}")
+    assert_close(yp, orc.gemm_w4a4(x, isc, c0, s0, g0), f"packed {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
+@pytest.mark.parametrize("M", [1, 8, 128, 1024])
+def test_gemm_packed_layers(orc, name, M):
+    w, _, _, (c, s, g) = _layer(name)
+    x = wl.activations(M, w.shape[1], seed=4)
+    _packed_matches(orc, x, np.float32(orc.global_scale(x)), c, s, g, f"packed {name} M={M}")
+
+
 # ------------------------------------------------------- W4A16 over any M --
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (6, 200, 8192), (9, 200, 256), (37, 200, 256),
