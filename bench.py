@@ -2,7 +2,7 @@
 
 One step = one pass over every kernel of the path on its full-size synthetic
 workload: dynamic quantize and dequantize of a 65536 x 6144 heavy-tailed bf16
-tensor; the W4A16 GEMV at batch 1, 2, 4, 8 on o_proj (6144 x 16384) and
+tensor, and its columnwise quantization and transposed dequantization; the W4A16 GEMV at batch 1, 2, 4, 8 on o_proj (6144 x 16384) and
 q_b_proj (16384 x 2048); the W4A4 GEMM (from bf16 and from a pre-packed
 activation) and the W4A16 GEMM at M in {1, 8, ..., 4096} on both shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
 6144, intermediate 2048) in W4A16 and W4A4 mode.  Inputs are resident in HBM
@@ -260,6 +260,21 @@ def main():
         progress("quantize workload ready")
         rows.append(Row("dequantize_65536x6144", [lambda: check(L.nvfp4_dequantize(*dargs), "dequantize")], 3, keep=qkeep,
                         nbytes=n * (0.5625 + 2), info={"bound": "hbm"}))
+        # the Dgrad layouts: the columnwise copy (NVFP4 of x^T) and the rowwise
+        # copy dequantized to bf16 and transposed
+        ct = torch.empty((C, R // 2), dtype=torch.uint8, device=dev)
+        st_ = torch.empty((C, R // 16), dtype=torch.uint8, device=dev)
+        gt = torch.empty(4, dtype=torch.float32, device=dev)
+        yt = torch.empty((C, R), dtype=torch.int16, device=dev)
+        cargs = (P(xq), R, C, None, P(ct), P(st_), P(gt), P(qws), qws.numel(), sptr)
+        targs = (P(qc), P(qs), P(qg), R, C, P(yt), sptr)
+        tkeep = (ct, st_, gt, yt) + qkeep
+        rows.append(Row("quantize_columnwise_65536x6144",
+                        [lambda: check(L.nvfp4_quantize_columnwise(*cargs), "quantize_columnwise")], 3, keep=tkeep,
+                        nbytes=n * (2 + 2 + 0.5 + 0.0625), info={"bound": "hbm", "bytes_model": "as quantize"}))
+        rows.append(Row("dequantize_transpose_65536x6144",
+                        [lambda: check(L.nvfp4_dequantize_transpose(*targs), "dequantize_transpose")], 3,
+                        keep=tkeep, nbytes=n * (0.5625 + 2), info={"bound": "hbm"}))
 
     # ---------------------------------------------------------------- GEMV --
     layers = {}
@@ -447,7 +462,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded numpy draws, bf16; NVFP4 weights quantized on the GPU)",
         "config": {"workload": "W4A16 batch-1 decode GEMV on NVFP4 o_proj [6144 x 16384]; step also runs "
-                               "quantize/dequantize 65536x6144, GEMV M=1..8 on o_proj and q_b_proj, "
+                               "quantize/dequantize (rowwise, columnwise, transposed) 65536x6144, GEMV M=1..8 on o_proj and q_b_proj, "
                                "W4A4 (bf16 and pre-packed activation) and W4A16 GEMM M=1..4096 on both, MoE T=4096 E=256 top-8 H=6144 I=2048",
                    "gpu": torch.cuda.get_device_name(0), "setup_s": round(setup_s, 1),
                    "timing": "HIP events around back-to-back launches enqueued behind a prefill kernel"},

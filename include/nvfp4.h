@@ -102,6 +102,33 @@ int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const floa
                          int64_t rows, int64_t cols, uint16_t* y, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The Dgrad layouts ("Getting GLM-5.2 NVFP4 Post-Training off the ground",
+ * "Going deeper" and "The bottom line"): Dgrad, dX = dY * W, contracts the
+ * weight over its output axis, and NVFP4 blocks must run along the
+ * contraction axis, so the rowwise copy's scales cannot serve it.
+ *
+ * nvfp4_quantize_columnwise: the columnwise copy, i.e. the NVFP4 quantization
+ * of x^T computed from the full-precision x (blocks of 16 along rows, same
+ * global scale and block rule as nvfp4_quantize, dynamic or static).
+ * x bf16 [rows, cols] -> codes_t [cols, rows/2], scales_t [cols, rows/16],
+ * *global_scale.  rows % 16 == 0 (else SHAPE), cols % 8 == 0 (else
+ * UNSUPPORTED).  Workspace as nvfp4_quantize: nvfp4_quantize_workspace_size
+ * (rows, cols) bytes in dynamic mode, none in static mode.  Bit-identical to
+ * nvfp4_quantize of the transposed tensor.
+ *
+ * nvfp4_dequantize_transpose: the page's alternative, the rowwise copy
+ * dequantized to bf16 and transposed on the fly for a bf16 Dgrad:
+ * y_t[c, r] = bf16( fl(fl(q[r, c] * s[r, c/16]) * Sg) ), y_t bf16 [cols, rows]
+ * (the transpose of nvfp4_dequantize's output, bit for bit).  cols % 16 == 0
+ * (else SHAPE), rows % 8 == 0 (else UNSUPPORTED).  No workspace.
+ * ------------------------------------------------------------------------ */
+int32_t nvfp4_quantize_columnwise(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
+                                  uint8_t* codes_t, uint8_t* scales_t, float* global_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+int32_t nvfp4_dequantize_transpose(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                   int64_t rows, int64_t cols, uint16_t* y_t, void* stream);
+
+/* ------------------------------------------------------------------------
  * W4A16 decode GEMV  (model card "vroomfondel/glm-5.2-reap-504B-v2-W4A4",
  * "What this variant changes": batch-1 decode projections are weight-bandwidth
  * bound; "Kernel choice": the weight-only NVFP4 path.)

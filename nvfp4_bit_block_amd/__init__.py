@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "nvfp4_gemv_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P]),
             "nvfp4_gemm_w4a4_workspace_size": (SZ, [I64, I64, I64]),
             "nvfp4_gemm_w4a4": (I32, [P, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
+            "nvfp4_quantize_columnwise": (I32, [P, I64, I64, P, P, P, P, P, SZ, P]),
+            "nvfp4_dequantize_transpose": (I32, [P, P, P, I64, I64, P, P]),
             "nvfp4_gemm_w4a4_packed_workspace_size": (SZ, [I64, I64, I64]),
             "nvfp4_gemm_w4a4_packed": (I32, [P, P, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
             "nvfp4_gemm_w4a16_workspace_size": (SZ, [I64, I64, I64]),
@@ -165,6 +167,34 @@ def quantize(x, static_scale=None, codes=None, scales=None, global_scale=None, w
                                 _ptr(global_scale), _ptr(ws), 0 if ws is None else ws.numel(),
                                 _stream(stream)), "nvfp4_quantize")
     return codes, scales, global_scale
+
+
+def quantize_columnwise(x, static_scale=None, codes=None, scales=None, global_scale=None, ws=None,
+                        stream=None):
+    """nvfp4_quantize_columnwise: NVFP4 of x^T; returns (codes [C, R/2], scales [C, R/16], global [1])."""
+    x = _bf16(x)
+    rows, cols = x.shape
+    dev = x.device
+    codes = _empty((cols, rows // 2), torch.uint8, dev) if codes is None else codes
+    scales = _empty((cols, rows // 16), torch.uint8, dev) if scales is None else scales
+    global_scale = _empty((1,), torch.float32, dev) if global_scale is None else global_scale
+    sst = None if static_scale is None else _dev_scalar(static_scale, dev)
+    need = 0 if sst is not None else quantize_workspace_size(rows, cols)
+    if ws is None and need:
+        ws = workspace(need, dev)
+    _check(lib().nvfp4_quantize_columnwise(_ptr(x), rows, cols, _ptr(sst), _ptr(codes), _ptr(scales),
+                                           _ptr(global_scale), _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(stream)), "nvfp4_quantize_columnwise")
+    return codes, scales, global_scale
+
+
+def dequantize_transpose(codes, scales, global_scale, out=None, stream=None):
+    """nvfp4_dequantize_transpose: bf16 [C, R] transpose of the dequantized [R, C] tensor."""
+    rows, half = codes.shape
+    out = _empty((half * 2, rows), torch.bfloat16, codes.device) if out is None else out
+    _check(lib().nvfp4_dequantize_transpose(_ptr(codes), _ptr(scales), _ptr(global_scale), rows, half * 2,
+                                            _ptr(out), _stream(stream)), "nvfp4_dequantize_transpose")
+    return out
 
 
 def dequantize(codes, scales, global_scale, out=None, stream=None):

@@ -239,6 +239,51 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const floa
     return hip_status(launch_quantize_pack(a, s), "quantize pack");
 }
 
+int32_t nvfp4_quantize_columnwise(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
+                                  uint8_t* codes_t, uint8_t* scales_t, float* global_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows < 0 || cols < 0 || rows % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "quantize_columnwise: need rows, cols >= 0 and rows %% 16 == 0%s");
+    if (cols % 8 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "quantize_columnwise: cols must be a multiple of 8%s");
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!x || !codes_t || !scales_t || !global_scale)
+        return fail(NVFP4_ERR_NULL_ARG, "quantize_columnwise: x, codes, scales and global_scale are required%s");
+    if (!aligned16(x) || !aligned16(codes_t) || !aligned16(scales_t) || !aligned4(global_scale) ||
+        (static_scale && !aligned4(static_scale)) || (workspace && !aligned16(workspace)))
+        return fail(NVFP4_ERR_ALIGN, "quantize_columnwise: pointers must be 16-byte aligned%s");
+    const size_t need = static_scale ? 0 : nvfp4_quantize_workspace_size(rows, cols);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(NVFP4_ERR_WORKSPACE, "quantize_columnwise: dynamic mode needs nvfp4_quantize_workspace_size bytes%s");
+    hipStream_t s = as_stream(stream);
+    if (static_scale)
+        return hip_status(launch_quantize_cols(x, rows, cols, ScaleMode::kStatic, nullptr, 0, static_scale, codes_t,
+                                               scales_t, global_scale, s),
+                          "quantize_columnwise");
+    const int grid = amax_grid(rows * cols);
+    uint32_t* partial = reinterpret_cast<uint32_t*>(workspace);
+    int32_t st = hip_status(launch_amax_partial(x, rows * cols, partial, grid, s), "quantize_columnwise amax");
+    if (st) return st;
+    return hip_status(launch_quantize_cols(x, rows, cols, ScaleMode::kDynamic, partial, grid, nullptr, codes_t,
+                                           scales_t, global_scale, s),
+                      "quantize_columnwise");
+}
+
+int32_t nvfp4_dequantize_transpose(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                   int64_t rows, int64_t cols, uint16_t* y_t, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows < 0 || cols <= 0 || cols % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "dequantize_transpose: need rows >= 0, cols > 0 and cols %% 16 == 0%s");
+    if (rows % 8 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "dequantize_transpose: rows must be a multiple of 8%s");
+    if (rows == 0) return NVFP4_OK;
+    if (!codes || !scales || !global_scale || !y_t)
+        return fail(NVFP4_ERR_NULL_ARG, "dequantize_transpose: all pointers are required%s");
+    if (!aligned16(codes) || !aligned16(scales) || !aligned4(global_scale) || !aligned16(y_t))
+        return fail(NVFP4_ERR_ALIGN, "dequantize_transpose: pointers must be 16-byte aligned%s");
+    return hip_status(launch_dequantize_t(codes, scales, global_scale, rows, cols, y_t, as_stream(stream)),
+                      "dequantize_transpose");
+}
+
 int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                          int64_t rows, int64_t cols, uint16_t* y, void* stream) {
     g_last_error[0] = '\0';

@@ -58,6 +58,19 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
 hipError_t launch_expand_qs(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                             uint16_t* out, bool bf16, hipStream_t stream);
 
+// Columnwise NVFP4 (transpose.hip): x bf16 [rows, cols] -> codes_t [cols,
+// rows/2] and scales_t [cols, rows/16], the rowwise quantization of x^T.
+// rows % 16 == 0, cols % 8 == 0.  Modes kDynamic (partials from
+// launch_amax_partial over x) and kStatic (*sg_ptr).
+hipError_t launch_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, ScaleMode mode,
+                                const uint32_t* partial, int npartial, const float* sg_ptr, uint8_t* codes_t,
+                                uint8_t* scales_t, float* global_out, hipStream_t stream);
+
+// Rowwise NVFP4 [rows, cols] -> bf16 y_t [cols, rows] = transpose of the
+// dequantized tensor.  rows % 8 == 0, cols % 16 == 0.
+hipError_t launch_dequantize_t(const uint8_t* codes, const uint8_t* scales, const float* sg_ptr, int64_t rows,
+                               int64_t cols, uint16_t* y_t, hipStream_t stream);
+
 // -------------------------------------------------------------------- GEMV --
 
 // y[m, n] = bf16(scale * sum_k s*q*x), scale = *g0 * (g1 ? *g1 : 1).

@@ -20,7 +20,7 @@ MIS = 4097        # misaligned
 def test_exports_every_header_symbol():
     L = ctypes.CDLL(nv.LIB_PATH)
     names = nv.header_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
 
@@ -54,6 +54,23 @@ def test_dequantize_validation():
     assert d(None, A, A, 4, 32, A, None) == NULL
     assert d(A, A, A, 4, 24, A, None) == SHAPE
     assert d(A, A, A, 4, 32, MIS, None) == ALIGN
+    assert d(A, A, A, 0, 32, A, None) == OK
+
+
+def test_columnwise_and_transpose_validation():
+    L = nv.lib()
+    q = L.nvfp4_quantize_columnwise
+    assert q(None, 32, 16, None, A, A, A, A, 1 << 20, None) == NULL
+    assert q(A, 24, 16, None, A, A, A, A, 1 << 20, None) == SHAPE           # rows % 16
+    assert q(A, 32, 12, None, A, A, A, A, 1 << 20, None) == UNSUP           # cols % 8
+    assert q(A, 32, 16, None, MIS, A, A, A, 1 << 20, None) == ALIGN
+    assert q(A, 32, 16, None, A, A, A, None, 0, None) == WS                  # dynamic needs workspace
+    assert q(A, 0, 16, None, A, A, A, None, 0, None) == OK
+    d = L.nvfp4_dequantize_transpose
+    assert d(None, A, A, 8, 32, A, None) == NULL
+    assert d(A, A, A, 8, 24, A, None) == SHAPE                               # cols % 16
+    assert d(A, A, A, 12, 32, A, None) == UNSUP                              # rows % 8
+    assert d(A, A, A, 8, 32, MIS, None) == ALIGN
     assert d(A, A, A, 0, 32, A, None) == OK
 
 
