@@ -66,6 +66,8 @@ def _lib():
             "orc_gemm_w4a4": (None, [P, F, I64, I64, I64, P, P, F, P]),
             "orc_moe": (None, [I64, I64, I64, I64, I64, ctypes.c_int32, P, P, P,
                                P, P, P, P, P, P, P, P, P, P]),
+            "orc_moe_lora": (None, [I64, I64, I64, I64, I64, ctypes.c_int32, P, P, P,
+                                    P, P, P, P, P, P, P, P, I64, F, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -199,8 +201,14 @@ def gemm_w4a4(x_bf16, input_scale, w_codes, w_scales, w_global) -> np.ndarray:
 
 
 def moe(x_bf16, topk_ids, topk_w, w13_codes, w13_scales, w13_global, w2_codes, w2_scales,
-        w2_global, mode: int = 0, a13=None, a2=None, want_h: bool = False):
-    """Routed-expert MoE layer; returns out [T, H] fp64 (and h bf16 [T*k, I])."""
+        w2_global, mode: int = 0, a13=None, a2=None, want_h: bool = False, lora=None):
+    """Routed-expert MoE layer; returns out [T, H] fp64 (and h bf16 [T*k, I]).
+
+    ``lora`` (optional) is a dict with ``scale`` (float) and the bf16 adapter
+    tensors ``a13`` [r, H], ``b13`` [E, 2I, r], ``a2`` [r, I], ``b2`` [E, H, r];
+    either pair may be ``None`` (no adapter on that projection).  The overlay
+    follows ``orc_moe_lora`` in nvfp4_oracle.c.
+    """
     x = _c(x_bf16, np.uint16)
     ids = _c(topk_ids, np.int32)
     w = _c(topk_w, np.float32)
@@ -221,8 +229,23 @@ def moe(x_bf16, topk_ids, topk_w, w13_codes, w13_scales, w13_global, w2_codes, w
         a2 = _c(a2, np.float32)
     out = np.empty((T, H), np.float64)
     h = np.empty((T * k, I), np.uint16) if want_h else None
-    _lib().orc_moe(T, E, k, H, I, mode, _ptr(x), _ptr(ids), _ptr(w), _ptr(w13c), _ptr(w13s),
-                   _ptr(w13g), _ptr(w2c), _ptr(w2s), _ptr(w2g),
-                   _ptr(a13) if mode == 1 else None, _ptr(a2) if mode == 1 else None,
-                   _ptr(out), _ptr(h))
+    rank, scale, la13, lb13, la2, lb2 = 0, 0.0, None, None, None, None
+    if lora is not None:
+        if lora.get("a13") is not None:
+            la13 = _c(lora["a13"], np.uint16)
+            lb13 = _c(lora["b13"], np.uint16)
+            rank = la13.shape[0]
+            assert la13.shape == (rank, H) and lb13.shape == (E, 2 * I, rank)
+        if lora.get("a2") is not None:
+            la2 = _c(lora["a2"], np.uint16)
+            lb2 = _c(lora["b2"], np.uint16)
+            assert rank in (0, la2.shape[0])
+            rank = la2.shape[0]
+            assert la2.shape == (rank, I) and lb2.shape == (E, H, rank)
+        scale = float(np.float32(lora["scale"]))
+    _lib().orc_moe_lora(T, E, k, H, I, mode, _ptr(x), _ptr(ids), _ptr(w), _ptr(w13c), _ptr(w13s),
+                        _ptr(w13g), _ptr(w2c), _ptr(w2s), _ptr(w2g),
+                        _ptr(a13) if mode == 1 else None, _ptr(a2) if mode == 1 else None,
+                        rank, scale, _ptr(la13), _ptr(lb13), _ptr(la2), _ptr(lb2),
+                        _ptr(out), _ptr(h))
     return (out, h) if want_h else out

@@ -306,12 +306,26 @@ ORC_API void orc_gemm_w4a4(const uint16_t* x, float input_scale, int64_t M, int6
  *   out[t] = sum_j w[t, j] * y   (fp64, j in order)
  * Weights per expert: w13 [E, 2I, H] and w2 [E, H, I] NVFP4 with one global
  * scale per expert tensor.  h_out (optional) receives h as bf16 [T*k, I].
- * Each expert is dequantized once, only if some token uses it. */
-ORC_API void orc_moe(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, int32_t mode,
-                     const uint16_t* x, const int32_t* ids, const float* w,
-                     const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_global,
-                     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_global,
-                     const float* a13, const float* a2, double* out, uint16_t* h_out) {
+ * Each expert is dequantized once, only if some token uses it.
+ *
+ * Optional bf16 LoRA overlay on the experts ([P1] "Going deeper" ->
+ * the rollout-engine passage: rank-64 bf16 LoRA on the MLP, applied to the
+ * NVFP4 routed experts by a non-fused MoE-LoRA path, with one LoRA-A shared
+ * by all experts and a LoRA-B per expert).  Rank r, multiplier `scale`:
+ *   z13 = bf16(A13 . x_t)              A13 bf16 [r, H]   (bf16 x, both modes)
+ *   g, u += scale * (B13_e . z13)      B13 bf16 [E, 2I, r], gate rows first
+ *   z2  = bf16(A2 . h)                 A2  bf16 [r, I]   (bf16 h, both modes)
+ *   y   += scale * (B2_e . z2)         B2  bf16 [E, H, r]
+ * each dot product in fp64; a projection whose A (and B) is NULL has no
+ * adapter.  The delta is added before the activation (gate/up) and before
+ * the weighted combine (down). */
+ORC_API void orc_moe_lora(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, int32_t mode,
+                          const uint16_t* x, const int32_t* ids, const float* w,
+                          const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_global,
+                          const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_global,
+                          const float* a13, const float* a2, int64_t rank, float scale,
+                          const uint16_t* lora_a13, const uint16_t* lora_b13, const uint16_t* lora_a2,
+                          const uint16_t* lora_b2, double* out, uint16_t* h_out) {
     const int64_t slots = T * topk;
     for (int64_t i = 0; i < T * H; i++) out[i] = 0.0;
     double* y_all = (double*)calloc((size_t)slots * (size_t)H, sizeof(double));
@@ -343,11 +357,32 @@ ORC_API void orc_moe(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, i
             } else {
                 for (int64_t k = 0; k < H; k++) xh[k] = orc_bf16_to_f32(x[t * H + k]);
             }
+            float* z = (float*)malloc(sizeof(float) * (size_t)(rank > 0 ? rank : 1));
+            if (lora_a13) {
+                for (int64_t q = 0; q < rank; q++) {
+                    double acc = 0.0;
+                    for (int64_t k = 0; k < H; k++)
+                        acc += (double)orc_bf16_to_f32(lora_a13[q * H + k]) *
+                               (double)orc_bf16_to_f32(x[t * H + k]);
+                    z[q] = orc_bf16_to_f32(orc_f64_to_bf16(acc));
+                }
+            }
             for (int64_t i = 0; i < I; i++) {
                 double g = 0.0, u = 0.0;
                 for (int64_t k = 0; k < H; k++) {
                     g += (double)w13d[i * H + k] * (double)xh[k];
                     u += (double)w13d[(I + i) * H + k] * (double)xh[k];
+                }
+                if (lora_a13) {
+                    const uint16_t* bg = lora_b13 + (e * 2 * I + i) * rank;
+                    const uint16_t* bu = lora_b13 + (e * 2 * I + I + i) * rank;
+                    double dg = 0.0, du = 0.0;
+                    for (int64_t q = 0; q < rank; q++) {
+                        dg += (double)orc_bf16_to_f32(bg[q]) * (double)z[q];
+                        du += (double)orc_bf16_to_f32(bu[q]) * (double)z[q];
+                    }
+                    g += (double)scale * dg;
+                    u += (double)scale * du;
                 }
                 double hv = g / (1.0 + exp(-g)) * u;
                 hb[i] = orc_f64_to_bf16(hv);
@@ -364,11 +399,26 @@ ORC_API void orc_moe(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, i
             } else {
                 for (int64_t i = 0; i < I; i++) hh[i] = orc_bf16_to_f32(hb[i]);
             }
+            if (lora_a2) {
+                for (int64_t q = 0; q < rank; q++) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < I; i++)
+                        acc += (double)orc_bf16_to_f32(lora_a2[q * I + i]) * (double)orc_bf16_to_f32(hb[i]);
+                    z[q] = orc_bf16_to_f32(orc_f64_to_bf16(acc));
+                }
+            }
             for (int64_t n = 0; n < H; n++) {
                 double acc = 0.0;
                 for (int64_t i = 0; i < I; i++) acc += (double)w2d[n * I + i] * (double)hh[i];
+                if (lora_a2) {
+                    const uint16_t* bn = lora_b2 + (e * H + n) * rank;
+                    double d = 0.0;
+                    for (int64_t q = 0; q < rank; q++) d += (double)orc_bf16_to_f32(bn[q]) * (double)z[q];
+                    acc += (double)scale * d;
+                }
                 y_all[p * H + n] = acc;
             }
+            free(z);
             free(xh);
             free(hh);
             free(hb);
@@ -382,4 +432,14 @@ ORC_API void orc_moe(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, i
     free(y_all);
     free(w13d);
     free(w2d);
+}
+
+/* The MoE layer without an adapter. */
+ORC_API void orc_moe(int64_t T, int64_t E, int64_t topk, int64_t H, int64_t I, int32_t mode,
+                     const uint16_t* x, const int32_t* ids, const float* w,
+                     const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_global,
+                     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_global,
+                     const float* a13, const float* a2, double* out, uint16_t* h_out) {
+    orc_moe_lora(T, E, topk, H, I, mode, x, ids, w, w13_codes, w13_scales, w13_global, w2_codes, w2_scales,
+                 w2_global, a13, a2, 0, 0.0f, NULL, NULL, NULL, NULL, out, h_out);
 }

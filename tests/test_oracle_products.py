@@ -203,3 +203,119 @@ def test_moe_w4a4_single_expert_composition(orc):
     np.testing.assert_array_equal(wl.bf16_bits_to_f32(h).astype(np.float64), href)
     ref = orc.gemm_w4a4(h, a2[0], q[3][0], q[4][0], q[5][0])
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- MoE-LoRA --
+# The bf16 adapter adds scale * B_e (A v) to each expert projection, with
+# z = A v rounded to bf16.  Where z is exact in bf16 (ternary A over
+# power-of-two-grid inputs, or A selecting single inputs), the adapted expert
+# is the dense MLP with the merged weights W + scale * B_e A, a plain fp64
+# matmul.
+
+def _ternary_bf16(rng, shape):
+    return wl.to_bf16_bits(rng.integers(-1, 2, size=shape).astype(np.float32))
+
+
+def _grid_tokens(rng, T, H):
+    # multiples of 1/8 in [-1/2, 1/2]: a ternary combination of 64 of them is
+    # 1/8 times an integer of magnitude at most 256, exact in bf16
+    assert H <= 64
+    return wl.to_bf16_bits(rng.integers(-4, 5, size=(T, H)).astype(np.float32) / 8)
+
+
+def _selector(rank, n, rng):
+    a = np.zeros((rank, n), np.float32)
+    a[np.arange(rank), rng.choice(n, rank, replace=False)] = 1.0
+    return wl.to_bf16_bits(a)
+
+
+def _f(b):
+    return wl.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def test_moe_lora_merged_weights(orc):
+    """Routed experts with an adapter on both projections equal per-slot dense
+    MLPs with merged weights: a transposed operand, a swapped gate/up half of
+    B13, a wrong expert's B or a misplaced scale all break the equality."""
+    rng = np.random.default_rng(21)
+    T, E, k, H, I, r = 6, 4, 2, 64, 32, 8
+    w13b, w2b, w13f, w2f = _experts(rng, E, H, I)
+    q = _quant_experts(orc, w13b, w2b)
+    x = _grid_tokens(rng, T, H)
+    ids, w = wl.moe_routing(T, E, k, seed=22)
+    scale = 0.75
+    lora = {"a13": _ternary_bf16(rng, (r, H)), "b13": wl.normal_bf16(rng, (E, 2 * I, r), 0.05),
+            "a2": _selector(r, I, rng), "b2": wl.normal_bf16(rng, (E, H, r), 0.05), "scale": scale}
+    out = orc.moe(x, ids, w, *q, mode=0, lora=lora)
+    xf = _f(x)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            m13 = w13f[e] + scale * _f(lora["b13"][e]) @ _f(lora["a13"])
+            m2 = w2f[e] + scale * _f(lora["b2"][e]) @ _f(lora["a2"])
+            y, _ = _dense_mlp(xf[t:t + 1], m13, m2, I)
+            ref[t] += float(w[t, j]) * y[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_moe_lora_rounds_the_rank_intermediate_to_bf16(orc):
+    """With the base down projection zero and B2 = the identity on the first r
+    outputs, the layer returns scale * bf16(A2 h): the rank-r intermediate is
+    the bf16 rounding (RNE, torch's conversion) of the exact product."""
+    rng = np.random.default_rng(23)
+    T, E, H, I, r = 5, 1, 64, 32, 16
+    w13b, _, _, _ = _experts(rng, E, H, I)
+    w2b = np.zeros((E, H, I), np.uint16)
+    q = _quant_experts(orc, w13b, w2b)
+    x = wl.activations(T, H, seed=24)
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    b2 = np.zeros((E, H, r), np.float32)
+    b2[0, np.arange(r), np.arange(r)] = 1.0
+    lora = {"a13": None, "a2": wl.normal_bf16(rng, (r, I), 0.3), "b2": wl.to_bf16_bits(b2), "scale": 2.0}
+    out, h = orc.moe(x, ids, w, *q, mode=0, want_h=True, lora=lora)
+    exact = _f(h) @ _f(lora["a2"]).T
+    z = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(out[:, :r], 2.0 * z)
+    np.testing.assert_array_equal(out[:, r:], 0.0)
+
+
+def test_moe_lora_zero_b_is_the_base_layer(orc):
+    """An adapter whose B is all zero (its initial state) changes nothing, in
+    both modes, bit for bit."""
+    rng = np.random.default_rng(25)
+    T, E, k, H, I, r = 5, 3, 2, 64, 32, 16
+    w13b, w2b, _, _ = _experts(rng, E, H, I)
+    q = _quant_experts(orc, w13b, w2b)
+    x = wl.activations(T, H, seed=26)
+    ids, w = wl.moe_routing(T, E, k, seed=27)
+    lora = {"a13": wl.normal_bf16(rng, (r, H), 0.1), "b13": np.zeros((E, 2 * I, r), np.uint16),
+            "a2": wl.normal_bf16(rng, (r, I), 0.1), "b2": np.zeros((E, H, r), np.uint16), "scale": 3.0}
+    a13 = np.full(E, orc.global_scale(x) * 2, np.float32)
+    a2 = np.full(E, 0.01, np.float32)
+    for mode in (0, 1):
+        base = orc.moe(x, ids, w, *q, mode=mode, a13=a13, a2=a2)
+        got = orc.moe(x, ids, w, *q, mode=mode, a13=a13, a2=a2, lora=lora)
+        np.testing.assert_array_equal(got, base)
+
+
+def test_moe_lora_uses_the_bf16_activation_in_w4a4(orc):
+    """In W4A4 mode the adapter reads the bf16 tokens, not their NVFP4
+    quantization: with the base weights zero, the W4A4 and W4A16 layers are
+    the same function of x."""
+    rng = np.random.default_rng(28)
+    T, E, k, H, I, r = 4, 2, 2, 64, 32, 8
+    z13 = np.zeros((E, 2 * I, H), np.uint16)
+    z2 = np.zeros((E, H, I), np.uint16)
+    q = _quant_experts(orc, z13, z2)
+    x = wl.activations(T, H, seed=29)
+    ids, w = wl.moe_routing(T, E, k, seed=30)
+    lora = {"a13": wl.normal_bf16(rng, (r, H), 0.1), "b13": wl.normal_bf16(rng, (E, 2 * I, r), 0.1),
+            "a2": wl.normal_bf16(rng, (r, I), 0.1), "b2": wl.normal_bf16(rng, (E, H, r), 0.1), "scale": 1.0}
+    a13 = np.full(E, 1e-3, np.float32)    # a badly saturating activation scale
+    a2 = np.full(E, 1e-3, np.float32)
+    w16 = orc.moe(x, ids, w, *q, mode=0, lora=lora)
+    w4 = orc.moe(x, ids, w, *q, mode=1, a13=a13, a2=a2, lora=lora)
+    assert np.abs(w16).max() > 0
+    np.testing.assert_array_equal(w4, w16)

@@ -126,3 +126,22 @@ def moe_expert_weights_iter(E: int = MOE_E, H: int = MOE_H, I: int = MOE_I, seed
         for done in sorted(futs):
             w13, w2 = futs.pop(done).result()
             yield done, w13, w2
+
+
+MOE_LORA_RANK = 64
+
+
+def moe_lora(E: int = MOE_E, H: int = MOE_H, I: int = MOE_I, rank: int = MOE_LORA_RANK, seed: int = 56,
+             std: float = 0.02):
+    """bf16 LoRA adapter for the routed experts ("Getting GLM-5.2 NVFP4
+    Post-Training off the ground", "Going deeper": rank 64 on the MLP, one
+    LoRA-A shared by the experts, one LoRA-B per expert).  Every tensor is
+    ~ N(0, std) (a trained adapter, not the all-zero B of initialisation):
+    a13 [r, H], b13 [E, 2I, r] (gate rows first), a2 [r, I], b2 [E, H, r]."""
+    rng = np.random.default_rng(seed)
+    return {
+        "a13": normal_bf16(rng, (rank, H), std),
+        "b13": normal_bf16(rng, (E, 2 * I, rank), std),
+        "a2": normal_bf16(rng, (rank, I), std),
+        "b2": normal_bf16(rng, (E, H, rank), std),
+    }
