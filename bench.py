@@ -5,7 +5,8 @@ workload: dynamic quantize and dequantize of a 65536 x 6144 heavy-tailed bf16
 tensor, and its columnwise quantization and transposed dequantization; the W4A16 GEMV at batch 1, 2, 4, 8 on o_proj (6144 x 16384) and
 q_b_proj (16384 x 2048); the W4A4 GEMM (from bf16 and from a pre-packed
 activation) and the W4A16 GEMM at M in {1, 8, ..., 4096} on both shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
-6144, intermediate 2048) in W4A16 and W4A4 mode.  Inputs are resident in HBM
+6144, intermediate 2048) in W4A16 and W4A4 mode, with and without a rank-64
+bf16 LoRA on its experts.  Inputs are resident in HBM
 before timing starts.  Weight-streaming kernels cycle through enough weight
 copies that every launch reads its weights from HBM, not from the 256 MB
 last-level cache.
@@ -391,6 +392,29 @@ def main():
                             keep=(xm, ids_d, wts_d, w13c, w13s, w13g, w2c, w2s, w2g, a13, a2, out, ws),
                             flops=moe_flops, info={"T": T, "E": E, "top_k": k, "H": H, "I": I,
                                                    "bytes_model": "NVFP4 expert weights + x + out"}))
+        # the same layer with a rank-64 bf16 LoRA on every expert projection
+        # (one A shared by the experts, one B per expert)
+        R = wl.MOE_LORA_RANK
+        lo = {n: to_dev(v) for n, v in wl.moe_lora(E, H, I, rank=R, seed=56).items()}
+        lcs = nv.MoeLora(R, 1.0, lo["a13"].data_ptr(), lo["b13"].data_ptr(), lo["a2"].data_ptr(),
+                         lo["b2"].data_ptr())
+        lora_bytes = 2 * R * (H + I) + 2 * E * R * (2 * I + H)
+        lora_flops = 2.0 * R * (T * H + T * k * (2 * I + I + H))
+        for mode in (0, 1):
+            p = nv.MoeProblem(T, E, k, H, I, mode)
+            ws = nv.workspace(L.nvfp4_moe_lora_workspace_size(ctypes.byref(p), ctypes.byref(lcs)), dev)
+            tens = nv.MoeTensors(xm.data_ptr(), ids_d.data_ptr(), wts_d.data_ptr(), w13c.data_ptr(),
+                                 w13s.data_ptr(), w13g.data_ptr(), w2c.data_ptr(), w2s.data_ptr(),
+                                 w2g.data_ptr(), a13.data_ptr() if mode else None,
+                                 a2.data_ptr() if mode else None, out.data_ptr())
+            a = (ctypes.byref(p), ctypes.byref(tens), ctypes.byref(lcs), P(ws), ws.numel(), sptr)
+            call = (lambda a=a, p=p, tens=tens, ws=ws: check(L.nvfp4_moe_grouped_gemm_lora(*a), "moe lora"))
+            rows.append(Row(f"moe_{'w4a16' if mode == 0 else 'w4a4'}_lora_r{R}", [call], 1,
+                            nbytes=moe_bytes + lora_bytes,
+                            keep=(xm, ids_d, wts_d, w13c, w13s, w13g, w2c, w2s, w2g, a13, a2, out, ws, lo, lcs),
+                            flops=moe_flops + lora_flops,
+                            info={"T": T, "E": E, "top_k": k, "H": H, "I": I, "lora_rank": R,
+                                  "bytes_model": "NVFP4 expert weights + bf16 adapter + x + out"}))
 
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup

@@ -248,6 +248,39 @@ size_t nvfp4_moe_workspace_size(const nvfp4_moe_problem* p);
 int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tensors* t, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The same layer with a bf16 LoRA overlay on the routed experts ("Getting
+ * GLM-5.2 NVFP4 Post-Training off the ground", "Going deeper": a rank-64
+ * bf16 LoRA on the MLP of an NVFP4 base, applied to the routed experts by a
+ * non-fused MoE-LoRA path, with one LoRA-A shared by all experts and one
+ * LoRA-B per expert).  With r = rank and c = scale:
+ *   z13 = bf16(x[t] * a13^T)   (the bf16 token, in both modes)
+ *   [g | u] += c * (z13 * b13_e^T)          before the activation
+ *   z2  = bf16(h * a2^T)       (the bf16 h, in both modes)
+ *   y_slot  += c * (z2 * b2_e^T)            before the weighted combine
+ * products accumulated in fp32.  a13 bf16 [r, H] and b13 bf16 [E, 2I, r]
+ * (gate rows first, as in W13) adapt the gate/up projection; a2 bf16 [r, I]
+ * and b2 bf16 [E, H, r] the down projection.  Either pair may be NULL (no
+ * adapter there); a pair with one NULL member is NULL_ARG.  The adapter
+ * tensors are 16-byte aligned (ALIGN).  rank <= 0 is SHAPE; rank % 8 != 0 or
+ * rank > 128 is UNSUPPORTED.  lora == NULL runs nvfp4_moe_grouped_gemm.
+ * Workspace: nvfp4_moe_lora_workspace_size(p, lora) bytes (the layer's
+ * workspace plus z13 [T, r] and z2 [T*top_k, r] in bf16).
+ * ------------------------------------------------------------------------ */
+typedef struct nvfp4_moe_lora {
+    int64_t rank;          /* r */
+    float scale;           /* c, multiplies the adapter's product (alpha / r) */
+    const uint16_t* a13;   /* bf16 [r, H] or NULL */
+    const uint16_t* b13;   /* bf16 [E, 2I, r] or NULL */
+    const uint16_t* a2;    /* bf16 [r, I] or NULL */
+    const uint16_t* b2;    /* bf16 [E, H, r] or NULL */
+} nvfp4_moe_lora;
+
+size_t nvfp4_moe_lora_workspace_size(const nvfp4_moe_problem* p, const nvfp4_moe_lora* lora);
+int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_tensors* t,
+                                    const nvfp4_moe_lora* lora, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,6 +43,11 @@ class MoeTensors(ctypes.Structure):
         "w2_codes", "w2_scales", "w2_global", "a13_scale", "a2_scale", "out")]
 
 
+class MoeLora(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int64), ("scale", ctypes.c_float), ("a13", ctypes.c_void_p),
+                ("b13", ctypes.c_void_p), ("a2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
 def header_functions() -> list[str]:
     """Names of the entry points declared in include/nvfp4.h."""
     text = open(HEADER).read()
@@ -76,6 +81,9 @@ def lib() -> ctypes.CDLL:
             "nvfp4_moe_workspace_size": (SZ, [ctypes.POINTER(MoeProblem)]),
             "nvfp4_moe_grouped_gemm": (I32, [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors),
                                              P, SZ, P]),
+            "nvfp4_moe_lora_workspace_size": (SZ, [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeLora)]),
+            "nvfp4_moe_grouped_gemm_lora": (I32, [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors),
+                                                  ctypes.POINTER(MoeLora), P, SZ, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -143,6 +151,27 @@ def gemm_w4a16_workspace_size(M: int, N: int, K: int) -> int:
 def moe_workspace_size(T, E, top_k, H, I, mode) -> int:
     p = MoeProblem(T, E, top_k, H, I, mode)
     return int(lib().nvfp4_moe_workspace_size(ctypes.byref(p)))
+
+
+def _moe_lora(lora) -> MoeLora | None:
+    """dict(scale=..., a13=, b13=, a2=, b2=) of bf16 device tensors (either
+    pair may be None) -> the C struct; the rank is read off the A tensors."""
+    if lora is None:
+        return None
+    rank = 0
+    for name in ("a13", "a2"):
+        if lora.get(name) is not None:
+            rank = lora[name].shape[0]
+    if lora.get("rank") is not None:
+        rank = int(lora["rank"])
+    return MoeLora(rank, float(lora["scale"]), *[None if lora.get(n) is None else _bf16(lora[n]).data_ptr()
+                                                 for n in ("a13", "b13", "a2", "b2")])
+
+
+def moe_lora_workspace_size(T, E, top_k, H, I, mode, lora) -> int:
+    p = MoeProblem(T, E, top_k, H, I, mode)
+    c = _moe_lora(lora)
+    return int(lib().nvfp4_moe_lora_workspace_size(ctypes.byref(p), None if c is None else ctypes.byref(c)))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -262,7 +291,10 @@ def gemm_w4a16(x, w_codes, w_scales, w_global, out=None, ws=None, stream=None):
 
 def moe_grouped_gemm(x, topk_ids, topk_weights, w13_codes, w13_scales, w13_global, w2_codes,
                      w2_scales, w2_global, mode=MODE_W4A16, a13_scale=None, a2_scale=None,
-                     out=None, ws=None, stream=None):
+                     out=None, ws=None, stream=None, lora=None):
+    """The routed-expert layer; ``lora`` (optional) is a dict with ``scale``
+    and the bf16 adapter tensors ``a13``/``b13`` and ``a2``/``b2`` (either
+    pair may be None) and runs nvfp4_moe_grouped_gemm_lora."""
     x = _bf16(x)
     T, H = x.shape
     k = topk_ids.shape[1]
@@ -271,11 +303,18 @@ def moe_grouped_gemm(x, topk_ids, topk_weights, w13_codes, w13_scales, w13_globa
     dev = x.device
     out = _empty((T, H), torch.bfloat16, dev) if out is None else out
     p = MoeProblem(T, E, k, H, I, mode)
+    c = _moe_lora(lora)
     if ws is None:
-        ws = workspace(lib().nvfp4_moe_workspace_size(ctypes.byref(p)), dev)
+        n = (lib().nvfp4_moe_workspace_size(ctypes.byref(p)) if c is None else
+             lib().nvfp4_moe_lora_workspace_size(ctypes.byref(p), ctypes.byref(c)))
+        ws = workspace(n, dev)
     t = MoeTensors(*[None if v is None else v.data_ptr() for v in (
         x, topk_ids, topk_weights, w13_codes, w13_scales, w13_global, w2_codes, w2_scales,
         w2_global, a13_scale, a2_scale, out)])
-    _check(lib().nvfp4_moe_grouped_gemm(ctypes.byref(p), ctypes.byref(t), _ptr(ws), ws.numel(),
-                                        _stream(stream)), "nvfp4_moe_grouped_gemm")
+    if c is None:
+        _check(lib().nvfp4_moe_grouped_gemm(ctypes.byref(p), ctypes.byref(t), _ptr(ws), ws.numel(),
+                                            _stream(stream)), "nvfp4_moe_grouped_gemm")
+    else:
+        _check(lib().nvfp4_moe_grouped_gemm_lora(ctypes.byref(p), ctypes.byref(t), ctypes.byref(c), _ptr(ws),
+                                                 ws.numel(), _stream(stream)), "nvfp4_moe_grouped_gemm_lora")
     return out

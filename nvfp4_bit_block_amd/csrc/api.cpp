@@ -145,10 +145,11 @@ constexpr int kMoeBM = 128;
 
 struct MoeLayout {
     size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0;
-    size_t xq = 0, hq = 0, h = 0, y = 0, total = 0;
+    size_t xq = 0, hq = 0, h = 0, y = 0, z13 = 0, z2 = 0, total = 0;
 };
 
-MoeLayout layout_moe(const nvfp4_moe_problem& p) {
+// lora_rank > 0 adds the bf16 rank-r projections z13 [T, r] and z2 [S, r].
+MoeLayout layout_moe(const nvfp4_moe_problem& p, int64_t lora_rank = 0) {
     MoeLayout l;
     const size_t S = (size_t)(p.T * p.top_k);
     size_t off = 0;
@@ -164,6 +165,10 @@ MoeLayout layout_moe(const nvfp4_moe_problem& p) {
     }
     l.h = off; off += align_up(S * (size_t)p.I * 2);
     l.y = off; off += align_up(S * (size_t)p.H * 4);
+    if (lora_rank > 0) {
+        l.z13 = off; off += align_up((size_t)p.T * (size_t)lora_rank * 2);
+        l.z2 = off; off += align_up(S * (size_t)lora_rank * 2);
+    }
     l.total = off;
     return l;
 }
@@ -449,8 +454,20 @@ size_t nvfp4_moe_workspace_size(const nvfp4_moe_problem* p) {
     return layout_moe(*p).total;
 }
 
+size_t nvfp4_moe_lora_workspace_size(const nvfp4_moe_problem* p, const nvfp4_moe_lora* lora) {
+    if (!p || p->T < 0 || p->E <= 0 || p->top_k <= 0 || p->H <= 0 || p->I <= 0) return 0;
+    if (lora && lora->rank <= 0) return 0;
+    return layout_moe(*p, lora ? lora->rank : 0).total;
+}
+
 int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tensors* t, void* workspace,
                                size_t workspace_bytes, void* stream) {
+    return nvfp4_moe_grouped_gemm_lora(p, t, nullptr, workspace, workspace_bytes, stream);
+}
+
+int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_tensors* t,
+                                    const nvfp4_moe_lora* lora, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     g_last_error[0] = '\0';
     if (!p || !t) return fail(NVFP4_ERR_NULL_ARG, "moe: problem and tensors are required%s");
     if (p->T < 0 || p->E <= 0 || p->top_k <= 0 || p->H <= 0 || p->I <= 0 || p->H % 16 || p->I % 16 ||
@@ -459,6 +476,11 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     if (p->H % 64 || p->I % 64) return fail(NVFP4_ERR_UNSUPPORTED, "moe: H and I must be multiples of 64%s");
     if (p->E > 4096) return fail(NVFP4_ERR_UNSUPPORTED, "moe: at most 4096 experts%s");
     if (p->T * p->top_k > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "moe: too many slots%s");
+    if (lora) {
+        if (lora->rank <= 0) return fail(NVFP4_ERR_SHAPE, "moe lora: rank must be positive%s");
+        if (lora->rank % 8 || lora->rank > 128)
+            return fail(NVFP4_ERR_UNSUPPORTED, "moe lora: rank must be a multiple of 8 and at most 128%s");
+    }
     {
         // the GEMM kernels address each operand through one buffer resource
         const int64_t S = p->T * p->top_k;
@@ -480,10 +502,19 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         if (!aligned4(q)) return fail(NVFP4_ERR_ALIGN, "moe: fp32/int32 arrays must be 4-byte aligned%s");
     if (p->mode == 1 && (!aligned4(t->a13_scale) || !aligned4(t->a2_scale)))
         return fail(NVFP4_ERR_ALIGN, "moe: fp32/int32 arrays must be 4-byte aligned%s");
+    const bool lora13 = lora && (lora->a13 || lora->b13), lora2 = lora && (lora->a2 || lora->b2);
+    if (lora && ((lora13 && (!lora->a13 || !lora->b13)) || (lora2 && (!lora->a2 || !lora->b2))))
+        return fail(NVFP4_ERR_NULL_ARG, "moe lora: a13/b13 and a2/b2 are given in pairs%s");
+    if (lora) {
+        const void* adapters[] = {lora->a13, lora->b13, lora->a2, lora->b2};
+        for (const void* q : adapters)
+            if (q && !aligned16(q)) return fail(NVFP4_ERR_ALIGN, "moe lora: adapter tensors must be 16-byte aligned%s");
+    }
     if (workspace && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "moe: workspace must be 16-byte aligned%s");
-    const MoeLayout l = layout_moe(*p);
+    const MoeLayout l = layout_moe(*p, lora ? lora->rank : 0);
     if (!workspace || workspace_bytes < l.total)
-        return fail(NVFP4_ERR_WORKSPACE, "moe: workspace smaller than nvfp4_moe_workspace_size%s");
+        return fail(NVFP4_ERR_WORKSPACE, lora ? "moe: workspace smaller than nvfp4_moe_lora_workspace_size%s"
+                                              : "moe: workspace smaller than nvfp4_moe_workspace_size%s");
 
     hipStream_t s = as_stream(stream);
     const int64_t S = p->T * p->top_k;
@@ -543,7 +574,21 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
         g1.a_div = (int32_t)p->top_k;
         g1.a_src_rows = p->T;
     }
-    st = hip_status(launch_gemm_a16(g1, af, Epi::kMoeGateUp, tile, grid_m, s), "moe gemm1");
+    if (lora13) {
+        // LoRA on gate/up: z13 = bf16(x A13^T) per token; the epilogue adds
+        // scale * z13[token] B13_e^T before the activation
+        uint16_t* z13 = at<uint16_t>(workspace, l.z13);
+        st = hip_status(launch_lora_a(t->x, p->T, p->H, lora->a13, (int)lora->rank, z13, s), "moe lora a13");
+        if (st) return st;
+        g1.lora_z = z13;
+        g1.lora_rows = perm;
+        g1.lora_div = (int32_t)p->top_k;
+        g1.lora_b = lora->b13;
+        g1.lora_rank = (int32_t)lora->rank;
+        g1.lora_scale = lora->scale;
+    }
+    st = hip_status(launch_gemm_a16(g1, af, lora13 ? Epi::kMoeGateUpLora : Epi::kMoeGateUp, tile, grid_m, s),
+                    "moe gemm1");
     if (st) return st;
 
     // GEMM 2: Y = h^ W2^T (fp32, per slot row)
@@ -578,7 +623,18 @@ int32_t nvfp4_moe_grouped_gemm(const nvfp4_moe_problem* p, const nvfp4_moe_tenso
     } else {
         g2.a = h;
     }
-    st = hip_status(launch_gemm_a16(g2, af, Epi::kMoeDown, tile, grid_m, s), "moe gemm2");
+    if (lora2) {
+        // LoRA on down: z2 = bf16(h A2^T) per slot row (expert-sorted, like h)
+        uint16_t* z2 = at<uint16_t>(workspace, l.z2);
+        st = hip_status(launch_lora_a(h, S, p->I, lora->a2, (int)lora->rank, z2, s), "moe lora a2");
+        if (st) return st;
+        g2.lora_z = z2;
+        g2.lora_b = lora->b2;
+        g2.lora_rank = (int32_t)lora->rank;
+        g2.lora_scale = lora->scale;
+    }
+    st = hip_status(launch_gemm_a16(g2, af, lora2 ? Epi::kMoeDownLora : Epi::kMoeDown, tile, grid_m, s),
+                    "moe gemm2");
     if (st) return st;
     return hip_status(launch_moe_combine(Y, inv, t->topk_weights, p->T, (int32_t)p->top_k, p->H, t->out, s),
                       "moe combine");

@@ -113,7 +113,9 @@ void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN>;
     using Op = typename OpOf<AF>::T;
     constexpr int BM = C::BM, BN = C::BN, WTM = C::WTM, WTN = C::WTN;
-    static_assert(EP != Epi::kMoeGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
+    constexpr bool kGateUp = EP == Epi::kMoeGateUp || EP == Epi::kMoeGateUpLora;
+    constexpr bool kLora = EP == Epi::kMoeGateUpLora || EP == Epi::kMoeDownLora;
+    static_assert(!kGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
     __shared__ __align__(16) uint8_t smem[2 * C::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -173,7 +175,25 @@ void k_gemm_a16(GemmArgs g) {
     const int ksteps = (int)(g.K / 64);
     const int per = (ksteps + g.ksplit - 1) / g.ksplit;
     const int kc0 = __builtin_amdgcn_readfirstlane(kz * per);
-    const int nsteps = __builtin_amdgcn_readfirstlane(max(0, min(ksteps - kc0, per)));
+    int nsteps = __builtin_amdgcn_readfirstlane(max(0, min(ksteps - kc0, per)));
+    const int gi = g.groups > 0 ? grp : 0;
+    float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
+    // LoRA overlay: the accumulators start at (lora_scale / sc) * (Z Bg^T),
+    // so that the epilogue's sc * acc adds lora_scale * (Z Bg^T) to the
+    // weight product.  If that ratio is not finite (sc is zero or nearly),
+    // the weight product vanishes: the K loop is skipped and the epilogue
+    // multiplies Z Bg^T by lora_scale alone.
+    float lora_mul = 0.0f;
+    if constexpr (kLora) {
+        const float ratio = g.lora_scale / sc;
+        if (fabsf(ratio) <= 3.402823466e38f) {
+            lora_mul = ratio;
+        } else {
+            nsteps = 0;
+            lora_mul = 1.0f;
+            sc = g.lora_scale;
+        }
+    }
 
     const uint32_t KB = (uint32_t)(g.K / 2), KS = (uint32_t)(g.K / 16), KA = (uint32_t)(g.K * 2);
     // A: 16-bit rows, optionally gathered, one resource over the source tensor
@@ -182,24 +202,9 @@ void k_gemm_a16(GemmArgs g) {
     const Rsrc rb_c = make_rsrc(g.b_codes + (int64_t)grp * g.N * KB, (uint64_t)g.N * KB);
     const Rsrc rb_s = make_rsrc(g.b_scales + (int64_t)grp * g.N * KS, (uint64_t)g.N * KS);
 
-    // ---- this thread's copy assignments (fixed for the whole K loop)
-    // A: chunk p = tid + NT * u -> row p / 8, 16-byte chunk p % 8 of the row's step
-    uint32_t va[C::A_PER_T], la[C::A_PER_T];
-#pragma unroll
-    for (int u = 0; u < C::A_PER_T; ++u) {
-        const int p = tid + C::NT * u, r = p >> 3, cc = p & 7;
-        const int64_t row = row_beg + r;
-        uint32_t v = kOob;
-        if (row < row_end) {
-            const int64_t src = g.a_rows ? (int64_t)(g.a_rows[row] / g.a_div) : row;
-            v = (uint32_t)(src * KA) + 16u * cc;
-        }
-        va[u] = v;
-        la[u] = r * kRowA + 16 * cc;
-    }
     // Global column of tile column n (or -1 past the end).
     auto b_col = [&](int n) -> int64_t {
-        if constexpr (EP == Epi::kMoeGateUp) {
+        if constexpr (kGateUp) {
             // column block j of wave w: gate columns for j < TN/2, the matching
             // up columns (I further) for j >= TN/2
             const int w = n / WTN, j = (n % WTN) / 32, cc = n % 32;
@@ -212,6 +217,89 @@ void k_gemm_a16(GemmArgs g) {
             return col < g.N ? col : -1;
         }
     };
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // LoRA overlay (see lora_mul): one bf16 contraction of length R per 32x32
+    // block, Z rows against the group's B rows (the output columns of the
+    // weight rows of this tile, gate/up order included), read straight from
+    // global memory in the MFMA operand layout, 64 ranks at a time with the
+    // loads of all blocks in flight together.  It runs before the K loop's
+    // address set-up and first loads, while few registers are live; the other
+    // workgroups on the CU cover its one round trip to L2.
+    if constexpr (kLora) {
+        const int R = g.lora_rank;
+        const uint16_t* bg = g.lora_b + (int64_t)grp * g.N * R;
+        const uint16_t* bp[TN];
+        const uint16_t* zp[TM];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = b_col(wn * WTN + 32 * j + c32);
+            bp[j] = col >= 0 ? bg + col * R + 8 * hf : nullptr;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t row = row_beg + wm * WTM + 32 * i + c32;
+            zp[i] = nullptr;
+            if (row < row_end)
+                zp[i] = g.lora_z + (int64_t)(g.lora_rows ? g.lora_rows[row] / g.lora_div : (int32_t)row) * R + 8 * hf;
+        }
+        for (int q0 = 0; q0 < R; q0 += 64) {   // uniform trip count
+            u32x4 za[TM][4], zb[TN][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int q = q0 + 16 * u;
+                const bool in = q + 8 * hf < R;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    za[i][u] = u32x4{0, 0, 0, 0};
+                    if (zp[i] && in) za[i][u] = *reinterpret_cast<const u32x4*>(zp[i] + q);
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    zb[j][u] = u32x4{0, 0, 0, 0};
+                    if (bp[j] && in) zb[j][u] = *reinterpret_cast<const u32x4*>(bp[j] + q);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = mfma(__builtin_bit_cast(bf16x8, za[i][u]), __builtin_bit_cast(bf16x8, zb[j][u]),
+                                         acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] *= lora_mul;
+    }
+    // ---- this thread's copy assignments (fixed for the whole K loop)
+    // A: chunk p = tid + NT * u -> row p / 8, 16-byte chunk p % 8 of the row's step
+    // LDS offsets are one per-thread base plus compile-time steps, so that
+    // they cost one register each and the steps go into the instructions'
+    // offset fields.
+    uint32_t va[C::A_PER_T];
+    const uint32_t la0 = (uint32_t)((tid >> 3) * kRowA + 16 * (tid & 7));
+#pragma unroll
+    for (int u = 0; u < C::A_PER_T; ++u) {
+        const int p = tid + C::NT * u, r = p >> 3, cc = p & 7;
+        const int64_t row = row_beg + r;
+        uint32_t v = kOob;
+        if (row < row_end) {
+            const int64_t src = g.a_rows ? (int64_t)(g.a_rows[row] / g.a_div) : row;
+            v = (uint32_t)(src * KA) + 16u * cc;
+        }
+        va[u] = v;
+    }
     // B codes: chunk p = tid + NT * u (p < 2 BN) -> column p / 2, half p % 2
     uint32_t vbc[C::B_PER_T], lbc[C::B_PER_T];
 #pragma unroll
@@ -251,7 +339,7 @@ void k_gemm_a16(GemmArgs g) {
     auto store_step = [&](const StageRegs& r, int buf) {
         uint8_t* base = smem + buf * C::STAGE;
 #pragma unroll
-        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la[u]) = r.a[u];
+        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la0 + u * (C::NT / 8) * kRowA) = r.a[u];
 #pragma unroll
         for (int u = 0; u < C::B_PER_T; ++u)
             if (tid + C::NT * u < C::B_CHUNKS) *reinterpret_cast<uint4*>(base + lbc[u]) = r.b[u];
@@ -259,23 +347,12 @@ void k_gemm_a16(GemmArgs g) {
     };
 
     // ---- fragment addresses within a stage buffer
-    uint32_t fa[TM], fbc[TN], fbs[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = (wm * WTM + 32 * i + c32) * kRowA + 64 * hf;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = wn * WTN + 32 * j + c32;
-        fbc[j] = C::A_BYTES + n * kRowB + 16 * hf;
-        fbs[j] = C::A_BYTES + C::BC_BYTES + 4 * n;
-    }
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const uint32_t fa0 = (uint32_t)((wm * WTM + c32) * kRowA + 64 * hf);
+    const uint32_t fbc0 = (uint32_t)(C::A_BYTES + (wn * WTN + c32) * kRowB + 16 * hf);
+    const uint32_t fbs0 = (uint32_t)(C::A_BYTES + C::BC_BYTES + 4 * (wn * WTN + c32));
+    auto fa = [&](int i) { return fa0 + 32 * i * kRowA; };
+    auto fbc = [&](int j) { return fbc0 + 32 * j * kRowB; };
+    auto fbs = [&](int j) { return fbs0 + 128 * j; };
 
     // One K step from LDS buffer `buf`: the A fragments of MFMA group kk + 1
     // are requested before the MFMAs of group kk are issued (the scheduling
@@ -291,18 +368,18 @@ void k_gemm_a16(GemmArgs g) {
         f32x2 sb[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            cb[j] = *reinterpret_cast<const uint4*>(base + fbc[j]);
-            sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(base + fbs[j]) >> (16 * hf));
+            cb[j] = *reinterpret_cast<const uint4*>(base + fbc(j));
+            sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(base + fbs(j)) >> (16 * hf));
         }
         Op av[2][TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) av[0][i] = *reinterpret_cast<const Op*>(base + fa[i]);
+        for (int i = 0; i < TM; ++i) av[0][i] = *reinterpret_cast<const Op*>(base + fa(i));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (kk + 1 < 4) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    av[(kk + 1) & 1][i] = *reinterpret_cast<const Op*>(base + fa[i] + 16 * (kk + 1));
+                    av[(kk + 1) & 1][i] = *reinterpret_cast<const Op*>(base + fa(i) + 16 * (kk + 1));
             }
             Op bv[TN];
 #pragma unroll
@@ -348,15 +425,13 @@ void k_gemm_a16(GemmArgs g) {
         if (nmain + u < nsteps) step(nmain + u, stg[(u + 1) % PD]);
 
     // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32
-    const int gi = g.groups > 0 ? grp : 0;
-    const float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t row = row_beg + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
             if (row >= row_end) continue;
-            if constexpr (EP == Epi::kMoeGateUp) {
+            if constexpr (kGateUp) {
 #pragma unroll
                 for (int j = 0; j < TN / 2; ++j) {
                     const int64_t hcol = (int64_t)tn * (BN / 2) + wn * (WTN / 2) + 32 * j + c32;
@@ -392,8 +467,9 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     int64_t wgs;
     if (g.groups > 0) {
         // grid_m bounds the row tiles of all groups; surplus workgroups exit
-        const int64_t ncols = (EP == Epi::kMoeGateUp) ? g.half_n : g.N;
-        const int64_t bn = (EP == Epi::kMoeGateUp) ? C::BN / 2 : C::BN;
+        constexpr bool kGateUp = EP == Epi::kMoeGateUp || EP == Epi::kMoeGateUpLora;
+        const int64_t ncols = kGateUp ? g.half_n : g.N;
+        const int64_t bn = kGateUp ? C::BN / 2 : C::BN;
         g.grouped_ntiles = (int32_t)((ncols + bn - 1) / bn);
         wgs = (int64_t)g.grouped_ntiles * grid_m * g.ksplit;
         wgs = (wgs + 7) / 8 * 8;  // a multiple of 8 for the XCD renumbering
@@ -474,6 +550,12 @@ hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, 
         case Epi::kPartialF32: return launch_tile<AF, Epi::kPartialF32>(g, tile, grid_m, stream); \
         case Epi::kMoeGateUp: return launch_tile<AF, Epi::kMoeGateUp>(g, tile, grid_m, stream);   \
         case Epi::kMoeDown: return launch_tile<AF, Epi::kMoeDown>(g, tile, grid_m, stream);       \
+        case Epi::kMoeGateUpLora:                                                         \
+            if (tile != A16Tile::k128x128_w64x64) break;                                  \
+            return launch_cfg<2, 2, 2, 2, 2, AF, Epi::kMoeGateUpLora, 3>(g, grid_m, stream); \
+        case Epi::kMoeDownLora:                                                           \
+            if (tile != A16Tile::k128x128_w64x64) break;                                  \
+            return launch_cfg<2, 2, 2, 2, 2, AF, Epi::kMoeDownLora, 3>(g, grid_m, stream);   \
     }
     switch (afmt) {
         case AFmt::kF16: NVFP4_EPI(AFmt::kF16) break;

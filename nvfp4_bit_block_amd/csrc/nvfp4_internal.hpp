@@ -98,6 +98,8 @@ enum class Epi : int {
     kPartialF32 = 1,  // partial[split] = acc (split-K, reduced later)
     kMoeGateUp = 2,   // h = bf16(silu(g*scale) * (u*scale))
     kMoeDown = 3,     // Y = acc * scale (fp32)
+    kMoeGateUpLora = 4,  // kMoeGateUp with the LoRA overlay added before the activation
+    kMoeDownLora = 5,    // kMoeDown with the LoRA overlay
 };
 
 struct GemmArgs {
@@ -123,6 +125,17 @@ struct GemmArgs {
     int64_t ldo = 0;
     int32_t ksplit = 1;
     int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
+    // LoRA overlay (the kMoe*Lora epilogues, ksplit 1): the
+    // epilogue value of (row, col) becomes
+    //   acc * globals + lora_scale * sum_q Z[zrow, q] * Bg[col, q]
+    // with Z bf16 [*, lora_rank] (zrow = lora_rows ? lora_rows[row] / lora_div
+    // : row) and Bg bf16 [N, lora_rank] the group's slice of lora_b.
+    const uint16_t* lora_z = nullptr;
+    const int32_t* lora_rows = nullptr;
+    int32_t lora_div = 1;
+    const uint16_t* lora_b = nullptr;
+    int32_t lora_rank = 0;  // a multiple of 8
+    float lora_scale = 0.0f;
 };
 
 // GEMM tiles with a 16-bit A operand (gemm_a16.hip): f16 products q * s
@@ -148,6 +161,11 @@ hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, 
                            hipStream_t stream);
 
 // y[m, n] = bf16(scale * sum_s partial[s][m][n]), scale = *g0 * (g1 ? *g1 : 1)
+// Rank-r projection of LoRA's shared A (lora.hip): Z [rows, R] =
+// bf16(X [rows, K] * A [R, K]^T) with fp32 accumulation; K % 64 == 0,
+// R % 8 == 0, R <= 128.
+hipError_t launch_lora_a(const uint16_t* x, int64_t rows, int64_t K, const uint16_t* a, int R, uint16_t* z,
+                         hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
 

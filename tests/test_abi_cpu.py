@@ -20,7 +20,7 @@ MIS = 4097        # misaligned
 def test_exports_every_header_symbol():
     L = ctypes.CDLL(nv.LIB_PATH)
     names = nv.header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
 
@@ -149,3 +149,30 @@ def test_moe_validation():
     assert run(p, t_words, A, ws - 1) == WS     # 4-byte aligned fp32/int32 arrays pass the alignment check
     assert run(nv.MoeProblem(0, 8, 2, 256, 128, 0), t, None, 0) == OK
     assert run(nv.MoeProblem(0, 8, 2, 256, 128, 1), nv.MoeTensors(), None, 0) == OK
+
+
+def test_moe_lora_validation():
+    L = nv.lib()
+    p = nv.MoeProblem(64, 8, 2, 256, 128, 0)
+    t = nv.MoeTensors(*([A] * 9 + [None, None, A]))
+    lo = nv.MoeLora(64, 1.0, A, A, A, A)
+    base = L.nvfp4_moe_workspace_size(ctypes.byref(p))
+    ws = L.nvfp4_moe_lora_workspace_size(ctypes.byref(p), ctypes.byref(lo))
+    # the layer's workspace plus z13 [T, r] and z2 [T*k, r] in bf16 (256-byte aligned pieces)
+    assert ws >= base + 64 * 64 * 2 + 128 * 64 * 2
+    assert L.nvfp4_moe_lora_workspace_size(ctypes.byref(p), None) == base
+    run = lambda pp, tt, ll, w, n: L.nvfp4_moe_grouped_gemm_lora(
+        ctypes.byref(pp), ctypes.byref(tt), None if ll is None else ctypes.byref(ll), w, n, None)
+    assert run(p, t, lo, A, ws - 1) == WS
+    assert run(p, t, None, A, base - 1) == WS
+    assert run(p, t, nv.MoeLora(0, 1.0, A, A, A, A), A, ws) == SHAPE
+    assert run(p, t, nv.MoeLora(-8, 1.0, A, A, A, A), A, ws) == SHAPE
+    assert run(p, t, nv.MoeLora(12, 1.0, A, A, A, A), A, 1 << 40) == UNSUP    # rank % 8 != 0
+    assert run(p, t, nv.MoeLora(136, 1.0, A, A, A, A), A, 1 << 40) == UNSUP   # rank > 128
+    assert run(p, t, nv.MoeLora(64, 1.0, A, None, A, A), A, ws) == NULL       # a13 without b13
+    assert run(p, t, nv.MoeLora(64, 1.0, A, A, None, A), A, ws) == NULL       # b2 without a2
+    assert run(p, t, nv.MoeLora(64, 1.0, A, A, MIS, A), A, ws) == ALIGN
+    # one adapted projection is enough; the workspace check still comes last
+    assert run(p, t, nv.MoeLora(64, 1.0, None, None, A, A), A, ws - 1) == WS
+    assert run(p, t, nv.MoeLora(64, 1.0, A, A, None, None), A, ws - 1) == WS
+    assert run(nv.MoeProblem(0, 8, 2, 256, 128, 0), t, lo, None, 0) == OK

@@ -1,8 +1,10 @@
 """Seeded synthetic inputs shaped like the layers the pages describe.
 
 This module only draws random numbers and rounds them to bf16 storage; it
-holds none of the NVFP4 arithmetic (no scales, no codes, no products), so
-both the CPU oracle and the HIP path can take their inputs from it.
+holds none of the NVFP4 arithmetic (no scale computation, no encoding, no
+products), so both the CPU oracle and the HIP path can take their inputs
+from it.  ``random_nvfp4`` draws code and scale bytes directly, which needs
+none of that arithmetic either.
 
 Shapes and distributions:
   * "vroomfondel/glm-5.2-reap-504B-v2-W4A4" model card, "What this variant
@@ -145,3 +147,22 @@ def moe_lora(E: int = MOE_E, H: int = MOE_H, I: int = MOE_I, rank: int = MOE_LOR
         "a2": normal_bf16(rng, (rank, I), std),
         "b2": normal_bf16(rng, (E, H, rank), std),
     }
+
+
+def random_nvfp4(lead, rows: int, cols: int, seed: int, device, rms: float = 0.02):
+    """Random NVFP4 tensors [*lead, rows, cols] drawn as bytes on ``device``
+    with a seeded torch generator: codes uniform over all 256 byte values
+    (two E2M1 codes each), E4M3 scale bytes uniform in [0x30, 0x40)
+    (block scales in [0.5, 2)), and one fp32 global scale per leading index
+    set so that the element rms is about ``rms`` (uniform E2M1 codes have rms
+    2.93, the scales about 1.2).  Used where a full-size expert stack is
+    needed quickly: quantizing 256 drawn experts takes minutes on a host.
+    Returns (codes uint8 [*lead, rows, cols/2], scales uint8
+    [*lead, rows, cols/16], global f32 [*lead])."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    lead = tuple(lead)
+    codes = torch.randint(0, 256, lead + (rows, cols // 2), generator=g, device=device, dtype=torch.uint8)
+    scales = torch.randint(0x30, 0x40, lead + (rows, cols // 16), generator=g, device=device, dtype=torch.uint8)
+    glob = torch.full(lead, rms / (2.93 * 1.2), dtype=torch.float32, device=device)
+    return codes, scales, glob
