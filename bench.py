@@ -122,6 +122,67 @@ def traffic_parse(fetch_db, write_db):
     print(json.dumps(rec))
 
 
+def counter_probe(kind):
+    """Launch a plain 512 MiB copy three times, then the kernels of one row
+    three times, for a rocprofv3 --pmc pass (kind: quantize or gemm)."""
+    import torch
+    import nvfp4_bit_block_amd as nv
+    import workloads as wl
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    if kind == "quantize":
+        x = to_dev(wl.heavy_tailed(65536, 6144, seed=1))
+        ws = nv.workspace(nv.quantize_workspace_size(65536, 6144), dev)
+        run = lambda: nv.quantize(x, ws=ws)
+    elif kind == "gemm":
+        w, _ = wl.gemv_inputs("q_b_proj")
+        wq = nv.quantize(to_dev(w))
+        wo, _ = wl.gemv_inputs("o_proj")
+        woq = nv.quantize(to_dev(wo))
+        xs = {}
+        for name, K in (("q_b_proj", 2048), ("o_proj", 16384)):
+            x = to_dev(wl.activations(4096, K, seed=4))
+            isc = torch.empty(1, dtype=torch.float32, device=dev)
+            nv.quantize(x, global_scale=isc)
+            xs[name] = (x, isc)
+
+        def run():
+            nv.gemm_w4a4(xs["q_b_proj"][0], xs["q_b_proj"][1], *wq)
+            nv.gemm_w4a4(xs["o_proj"][0], xs["o_proj"][1], *woq)
+    else:
+        raise SystemExit(f"unknown counter probe {kind!r}")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    print(f"counter probe {kind} done", flush=True)
+
+
+def counter_report(dbs):
+    """Median per-dispatch value of every counter in rocprofv3 --pmc databases,
+    per kernel and launch shape (markdown)."""
+    import sqlite3
+    print("| kernel | grid | counter | dispatches | median per dispatch |")
+    print("|---|---|---|---|---|")
+    for db in dbs:
+        con = sqlite3.connect(db)
+        cols = {r[1] for r in con.execute("pragma table_info(counters_collection)")}
+        grid = next((c for c in ("grid_size", "grid_x", "grid_size_x") if c in cols), "0")
+        q = (f"select dispatch_id, kernel_name, {grid}, counter_name, sum(value) from counters_collection "
+             "group by dispatch_id, counter_name order by dispatch_id")
+        vals = {}
+        for _, k, grid, ctr, v in con.execute(q):
+            short = k.replace("(anonymous namespace)::", "").replace("nvfp4::", "")
+            short = short[5:].split(">(")[0] + ">" if short.startswith("void ") else short.split("(")[0]
+            vals.setdefault((short[:90], grid, ctr), []).append(v)
+        for (k, grid, ctr), v in vals.items():
+            print(f"| `{k}` | {grid} | {ctr} | {len(v)} | {float(np.median(v)):.6g} |")
+
+
 def trace_summary(db, filt):
     """Per-kernel durations from a rocprofv3 kernel-trace database, one row per
     kernel and launch shape, sorted by total time."""
@@ -171,6 +232,11 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch a plain 512 MiB copy and the batch-1 o_proj GEMV, three times each "
                          "(run this under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--counter-probe", choices=("quantize", "gemm"),
+                    help="only launch a plain 512 MiB copy, then the quantize of 65536 x 6144 or the W4A4 GEMM at "
+                         "M = 4096 on q_b_proj and o_proj, three times each (run under rocprofv3 --pmc)")
+    ap.add_argument("--counter-report", nargs="+", metavar="DB",
+                    help="median per-dispatch counter values of rocprofv3 --pmc databases (markdown)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "FILTER"),
                     help="print a markdown table of a rocprofv3 --kernel-trace database (kernels whose name "
                          "contains FILTER; '' for all library kernels)")
@@ -207,6 +273,12 @@ def main():
         return
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.counter_probe:
+        counter_probe(args.counter_probe)
+        return
+    if args.counter_report:
+        counter_report(args.counter_report)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
