@@ -526,6 +526,29 @@ def main():
             r.total_ms += e0.elapsed_time(e1)
             r.launches += r.reps
 
+    # Per-launch spread of the batch-1 GEMVs: one more pass with an event
+    # between consecutive launches (the event markers add a little time of
+    # their own, so the mean above stays the reported figure).
+    spread = {}
+    for r in rows:
+        if r.name not in ("gemv_w4a16_o_proj_M1", "gemv_w4a16_q_b_proj_M1"):
+            continue
+        sleeper.prefill(r)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(r.reps + 1)]
+        evs[0].record(stream)
+        for i in range(r.reps):
+            r.calls[r.k % len(r.calls)]()
+            r.k += 1
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(r.reps)])
+        spread[r.name] = {"marked_us_median": round(float(np.median(per)), 3),
+                          "marked_us_p10": round(float(np.percentile(per, 10)), 3),
+                          "marked_us_p90": round(float(np.percentile(per, 90)), 3),
+                          "marked_launches": int(r.reps),
+                          "marked_note": "per-launch times with an event marker between launches "
+                                         "(each marker adds a few us); for the spread, not the rate"}
+
     report = {}
     for r in rows:
         us = 1e3 * r.total_ms / max(r.launches, 1)
@@ -539,6 +562,7 @@ def main():
             d["TFLOPS"] = round(tf, 2)
             d["frac_mfma_f16_peak"] = round(tf / MFMA_F16_PEAK_TFLOPS, 4)
         d.update({k: v for k, v in r.info.items() if k not in ("M", "N", "K")})
+        d.update(spread.get(r.name, {}))
         report[r.name] = d
 
     head = report.get("gemv_w4a16_o_proj_M1")
