@@ -272,3 +272,40 @@ def test_moe_w4a4(orc, T, E, k, H, I):
                             a13_scale=dev(a13), a2_scale=dev(a2))
     torch.cuda.synchronize()
     assert_close(host_bf16_f32(y), ref, f"moe w4a4 T={T}")
+
+
+def _skewed_routing(counts, k, seed):
+    """Top-k ids with exact per-expert slot counts: the experts' slots laid
+    out in expert order and dealt column by column (token t takes slots t,
+    t + T, ...), which keeps a token's k experts distinct for these counts."""
+    L = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    T = len(L) // k
+    ids = np.ascontiguousarray(L.reshape(k, T).T)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    w = np.random.default_rng(seed).random((T, k)).astype(np.float32) + 0.1
+    return ids, (w / w.sum(1, keepdims=True)).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_moe_rows_beyond_full_tiles(orc, mode):
+    """Experts with more rows than one 128-row tile: 150, 160, 161, 129, 261
+    (three tiles) and 39 rows, so partly filled tiles follow full ones."""
+    counts = [150, 160, 161, 129, 261, 39]
+    k, H, I = 3, 256, 128
+    ids, wts = _skewed_routing(counts, k, seed=9)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=len(counts)), counts)
+    T, E = ids.shape[0], len(counts)
+    x, _, _, cw, gw = _moe_case(orc, 1, E, 1, H, I, seed=31)
+    x = wl.activations(T, H, seed=32)
+    if mode == 0:
+        ref = orc.moe(x, ids, wts, *cw, mode=0)
+        y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A16)
+    else:
+        _, h = orc.moe(x, ids, wts, *cw, mode=0, want_h=True)
+        a13 = np.full(E, orc.global_scale(x), np.float32)
+        a2 = np.full(E, orc.global_scale(h), np.float32)
+        ref = orc.moe(x, ids, wts, *cw, mode=1, a13=a13, a2=a2)
+        y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A4,
+                                a13_scale=dev(a13), a2_scale=dev(a2))
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), ref, f"moe skewed routing mode {mode}")
