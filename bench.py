@@ -124,7 +124,7 @@ def traffic_parse(fetch_db, write_db):
 
 def counter_probe(kind):
     """Launch a plain 512 MiB copy three times, then the kernels of one row
-    three times, for a rocprofv3 --pmc pass (kind: quantize or gemm)."""
+    three times, for a rocprofv3 --pmc pass (kind: quantize, gemm or moe)."""
     import torch
     import nvfp4_bit_block_amd as nv
     import workloads as wl
@@ -151,6 +151,30 @@ def counter_probe(kind):
         def run():
             nv.gemm_w4a4(xs["q_b_proj"][0], xs["q_b_proj"][1], *wq)
             nv.gemm_w4a4(xs["o_proj"][0], xs["o_proj"][1], *woq)
+    elif kind == "moe":
+        # the bench's MoE layer (T 4096, 256 experts, top-8, H 6144, I 2048)
+        T, E, k, H, I = wl.MOE_T, wl.MOE_E, wl.MOE_TOPK, wl.MOE_H, wl.MOE_I
+        ids, wts = wl.moe_routing(T, E, k, seed=5)
+        xm = to_dev(wl.moe_tokens(T, H, seed=55))
+        w13 = [torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev),
+               torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=dev),
+               torch.empty(E, dtype=torch.float32, device=dev)]
+        w2 = [torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev),
+              torch.empty((E, H, I // 16), dtype=torch.uint8, device=dev),
+              torch.empty(E, dtype=torch.float32, device=dev)]
+        for e, a, b in wl.moe_expert_weights_iter(E, H, I, seed=50, threads=16):
+            nv.quantize(to_dev(a), codes=w13[0][e], scales=w13[1][e], global_scale=w13[2][e:e + 1])
+            nv.quantize(to_dev(b), codes=w2[0][e], scales=w2[1][e], global_scale=w2[2][e:e + 1])
+        ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+        tmp = torch.empty(1, dtype=torch.float32, device=dev)
+        nv.quantize(xm, global_scale=tmp)
+        a13 = tmp.expand(E).contiguous()
+        a2 = torch.full((E,), 2.0 * H * 0.02 ** 2 * float(np.log(T * k * I)) / 2688.0, dtype=torch.float32,
+                        device=dev)
+
+        def run():
+            nv.moe_grouped_gemm(xm, ids_d, wts_d, *w13, *w2, mode=nv.MODE_W4A16)
+            nv.moe_grouped_gemm(xm, ids_d, wts_d, *w13, *w2, mode=nv.MODE_W4A4, a13_scale=a13, a2_scale=a2)
     else:
         raise SystemExit(f"unknown counter probe {kind!r}")
     torch.cuda.synchronize()
@@ -232,9 +256,10 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch a plain 512 MiB copy and the batch-1 o_proj GEMV, three times each "
                          "(run this under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
-    ap.add_argument("--counter-probe", choices=("quantize", "gemm"),
-                    help="only launch a plain 512 MiB copy, then the quantize of 65536 x 6144 or the W4A4 GEMM at "
-                         "M = 4096 on q_b_proj and o_proj, three times each (run under rocprofv3 --pmc)")
+    ap.add_argument("--counter-probe", choices=("quantize", "gemm", "moe"),
+                    help="only launch a plain 512 MiB copy, then the quantize of 65536 x 6144, the W4A4 GEMM at "
+                         "M = 4096 on q_b_proj and o_proj, or the MoE layer in both modes, three times each "
+                         "(run under rocprofv3 --pmc)")
     ap.add_argument("--counter-report", nargs="+", metavar="DB",
                     help="median per-dispatch counter values of rocprofv3 --pmc databases (markdown)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "FILTER"),
