@@ -410,7 +410,13 @@ int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, 
         return fail(NVFP4_ERR_WORKSPACE, "gemm_packed: workspace smaller than nvfp4_gemm_w4a4_packed_workspace_size%s");
     hipStream_t s = as_stream(stream);
     const GemmPlan p = plan_gemm(M, N, K);
-    // The packed activation is expanded to its exact products q * s, the
+    // Small M on the fixed GEMV layouts: the GEMV decodes the packed
+    // activation itself (one launch).
+    if (p.gemv && gemv_takes_packed((int)M, K))
+        return hip_status(launch_gemv_w4a4_packed(a_codes, a_scales, (int)M, N, K, w_codes, w_scales, w_global,
+                                                  a_global, y, s),
+                          "gemm_packed gemv");
+    // Otherwise the packed activation is expanded to its exact products q * s, the
     // operand form of both kernels (bf16 for the GEMV, f16 for the tiles);
     // the two global scales are applied after the contraction.
     uint16_t* xh = at<uint16_t>(workspace, l.xhat);

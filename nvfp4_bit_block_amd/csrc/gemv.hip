@@ -104,17 +104,23 @@ struct Frag {
 // across the wave with shuffles and, when KS > 1, across the group's waves
 // through LDS.
 //
+// With AP (the W4A4 product on a pre-packed activation) x points to the
+// activation's packed codes [M, K/2] and xs to its E4M3 scales [M, K/16]: each
+// lane decodes its slice to the exact products q * s as bf16 (the values the
+// expanded operand would hold), and g1 is the activation's global scale.
+//
 // With AQ (the W4A4 product at M = 1) x is the unquantized bf16 activation:
 // each lane NVFP4-encodes its slice under the static activation scale *g1
 // (the quantizer's block rule) and keeps the exact products q * s as bf16,
 // the operand the two-kernel path would read back from memory.
-template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false>
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false, bool AP = false>
 __global__ __launch_bounds__(THREADS) void k_gemv(const uint16_t* __restrict__ x, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ wc,
                                                    const uint8_t* __restrict__ ws,
                                                    const float* __restrict__ g0,
                                                    const float* __restrict__ g1,
-                                                   uint16_t* __restrict__ y) {
+                                                   uint16_t* __restrict__ y,
+                                                   const uint8_t* __restrict__ xs) {
     constexpr int kWavesPerBlock = THREADS / kWave;
     constexpr int kGroups = kWavesPerBlock / KS;
     static_assert(kWavesPerBlock % KS == 0, "row groups");
@@ -162,14 +168,32 @@ __global__ __launch_bounds__(THREADS) void k_gemv(const uint16_t* __restrict__ x
     if (my_iters > 0) load(f, gid);
 
     uint4 xr[M * NCH * 4];
+    if constexpr (AP) {
+        // chunk c of row m: 16 code bytes (two blocks) and their two scale bytes
+        const uint8_t* xc = reinterpret_cast<const uint8_t*>(x);
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint4* p = reinterpret_cast<const uint4*>(x + m * K + chunk(j) * 32);
+            for (int j = 0; j < NCH; ++j) {
+                const uint4 q = *reinterpret_cast<const uint4*>(xc + m * KB + chunk(j) * 16);
+                const uint32_t s2 = *reinterpret_cast<const uint16_t*>(xs + m * KS16 + chunk(j) * 2);
+                const float s0 = e4m3_to_f32(s2 & 0xFFu), s1 = e4m3_to_f32(s2 >> 8);
+                uint4* o = &xr[(m * NCH + j) * 4];
+                o[0] = fp4x8_scaled_bf16_bits(q.x, s0);
+                o[1] = fp4x8_scaled_bf16_bits(q.y, s0);
+                o[2] = fp4x8_scaled_bf16_bits(q.z, s1);
+                o[3] = fp4x8_scaled_bf16_bits(q.w, s1);
+            }
+    } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xr[(m * NCH + j) * 4 + i] = p[i];
-        }
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint4* p = reinterpret_cast<const uint4*>(x + m * K + chunk(j) * 32);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xr[(m * NCH + j) * 4 + i] = p[i];
+            }
+    }
     if constexpr (AQ) {
         const float sg = *g1, t = 6.0f * sg;
 #pragma unroll
@@ -306,16 +330,16 @@ constexpr int64_t kMaxLdsBytes = 64 * 1024;
 
 // Grid: about `blocks_per_cu` workgroups per CU on a 256-CU chip, never
 // more than there are row batches.
-template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false>
+template <int M, int NCH, int KS, int RW, int THREADS = kThreads, bool AQ = false, bool AP = false>
 hipError_t launch_cfg(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
                       const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
-                      int blocks_per_cu) {
+                      int blocks_per_cu, const uint8_t* xs = nullptr) {
     constexpr int64_t groups = (THREADS / kWave) / KS;
     const int64_t nbatch = (N + RW - 1) / RW;
     int64_t grid = min((int64_t)256 * blocks_per_cu, (nbatch + groups - 1) / groups);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, THREADS, AQ>), dim3((unsigned)grid), dim3(THREADS), 0, stream, x, N, K,
-                       wc, ws, g0, g1, y);
+    hipLaunchKernelGGL((k_gemv<M, NCH, KS, RW, THREADS, AQ, AP>), dim3((unsigned)grid), dim3(THREADS), 0, stream, x,
+                       N, K, wc, ws, g0, g1, y, xs);
     return hipGetLastError();
 }
 
@@ -330,18 +354,19 @@ hipError_t launch_any(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc
     return hipGetLastError();
 }
 
-template <int M, bool AQ = false>
+template <int M, bool AQ = false, bool AP = false>
 hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, const uint8_t* ws,
-                    const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
+                    const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
+                    const uint8_t* xs = nullptr) {
     const bool fits_lds = (int64_t)M * K * 2 <= kMaxLdsBytes;
     // measured on MI355X (o_proj 6144 x 16384 and q_b_proj 16384 x 2048):
     // K = 2048: one wave per row, four rows in flight, three workgroups per
     // CU (two for M > 4); K = 16384: eight waves split K (one 32-element
     // chunk per lane), four rows in flight, one 512-thread workgroup per CU
     if (K == 2048)
-        return launch_cfg<M, 1, 1, 4, kThreads, AQ>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2);
-    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512, AQ>(x, N, K, wc, ws, g0, g1, y, stream, 1);
-    if constexpr (AQ) return hipErrorNotSupported;
+        return launch_cfg<M, 1, 1, 4, kThreads, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2, xs);
+    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 1, xs);
+    if constexpr (AQ || AP) return hipErrorNotSupported;
     if (fits_lds) return launch_any<M, true>(x, N, K, wc, ws, g0, g1, y, stream);
     return launch_any<M, false>(x, N, K, wc, ws, g0, g1, y, stream);
 }
@@ -381,6 +406,28 @@ hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, cons
                             uint16_t* y, hipStream_t stream) {
     if (!gemv_quantizes_activation(M, K)) return hipErrorNotSupported;
     return launch_m<1, true>(x, N, K, wc, ws, w_global, input_scale, y, stream);
+}
+
+// The fixed chunk layouts decode a packed activation in registers; other K
+// expand it to q * s in memory first.
+bool gemv_takes_packed(int M, int64_t K) { return M >= 1 && M <= 8 && (K == 2048 || K == 16384); }
+
+hipError_t launch_gemv_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, int M, int64_t N, int64_t K,
+                                   const uint8_t* wc, const uint8_t* ws, const float* w_global,
+                                   const float* a_global, uint16_t* y, hipStream_t stream) {
+    if (!gemv_takes_packed(M, K)) return hipErrorNotSupported;
+    const uint16_t* xc = reinterpret_cast<const uint16_t*>(a_codes);
+    switch (M) {
+        case 1: return launch_m<1, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 2: return launch_m<2, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 3: return launch_m<3, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 4: return launch_m<4, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 5: return launch_m<5, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 6: return launch_m<6, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 7: return launch_m<7, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        case 8: return launch_m<8, false, true>(xc, N, K, wc, ws, w_global, a_global, y, stream, a_scales);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace nvfp4

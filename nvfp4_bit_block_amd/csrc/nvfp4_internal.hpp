@@ -88,6 +88,14 @@ hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, cons
                             const uint8_t* ws, const float* w_global, const float* input_scale,
                             uint16_t* y, hipStream_t stream);
 
+// W4A4 GEMV on a pre-packed activation (codes [M, K/2], scales [M, K/16],
+// global scale a_global), decoded in registers; for the M, K of
+// gemv_takes_packed(M, K), hipErrorNotSupported otherwise.
+bool gemv_takes_packed(int M, int64_t K);
+hipError_t launch_gemv_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, int M, int64_t N, int64_t K,
+                                   const uint8_t* wc, const uint8_t* ws, const float* w_global,
+                                   const float* a_global, uint16_t* y, hipStream_t stream);
+
 // -------------------------------------------------------------------- GEMM --
 
 // A operand formats: bf16 values, or f16 values that are the exact products

@@ -116,7 +116,7 @@ def _packed_matches(orc, x, isc, c, s, g, what):
     return yp
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (3, 200, 2048), (9, 200, 256), (37, 200, 256),
+@pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (3, 200, 2048), (5, 67, 16384), (9, 200, 256), (37, 200, 256),
                                    (130, 384, 512), (300, 136, 640)])
 def test_gemm_packed_shapes(orc, M, N, K):
     # quantize once (static), then the GEMM on codes and scales: the same bits
