@@ -15,6 +15,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteBatch = 8;
 constexpr int kMaxExperts = 4096;
 
 __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t* __restrict__ ids,
@@ -28,9 +29,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t* __re
     __shared__ int32_t cur[kMaxExperts];
     for (int e = threadIdx.x; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
-    for (int64_t p = threadIdx.x; p < slots; p += kRouteThreads) {
-        const int32_t e = ids[p];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    // the slot loops issue kRouteBatch id loads before their atomics, so a
+    // thread waits on memory once per batch rather than once per slot
+    for (int64_t p0 = threadIdx.x; p0 < slots; p0 += (int64_t)kRouteThreads * kRouteBatch) {
+        int32_t e[kRouteBatch];
+#pragma unroll
+        for (int u = 0; u < kRouteBatch; ++u) {
+            const int64_t p = p0 + (int64_t)u * kRouteThreads;
+            e[u] = p < slots ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kRouteBatch; ++u)
+            if (e[u] >= 0 && e[u] < E) atomicAdd(&cnt[e[u]], 1);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -46,15 +56,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t* __re
         tile_off[E] = t;
     }
     __syncthreads();
-    for (int64_t p = threadIdx.x; p < slots; p += kRouteThreads) {
-        const int32_t e = ids[p];
-        if (e >= 0 && e < E) {
-            const int32_t pos = atomicAdd(&cur[e], 1);
-            perm[pos] = (int32_t)p;
-            inv[p] = pos;
-            pos_group[pos] = e;
-        } else {
-            inv[p] = -1;
+    for (int64_t p0 = threadIdx.x; p0 < slots; p0 += (int64_t)kRouteThreads * kRouteBatch) {
+        int32_t e[kRouteBatch];
+#pragma unroll
+        for (int u = 0; u < kRouteBatch; ++u) {
+            const int64_t p = p0 + (int64_t)u * kRouteThreads;
+            e[u] = p < slots ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kRouteBatch; ++u) {
+            const int64_t p = p0 + (int64_t)u * kRouteThreads;
+            if (p >= slots) break;
+            if (e[u] >= 0 && e[u] < E) {
+                const int32_t pos = atomicAdd(&cur[e[u]], 1);
+                perm[pos] = (int32_t)p;
+                inv[p] = pos;
+                pos_group[pos] = e[u];
+            } else {
+                inv[p] = -1;
+            }
         }
     }
 }
