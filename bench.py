@@ -99,14 +99,14 @@ def traffic_parse(fetch_db, write_db):
            "traffic_bytes": round(total), "algorithmic_bytes": algo}
     lines = [
         "# HBM traffic: batch-1 W4A16 GEMV, o_proj 6144 x 16384", "",
-        "Commands (repository root on the MI355X box; two counter passes, then this file):", "",
+        "Commands (repository root on an MI355X; $OUT is an output directory; two counter passes, then this file):", "",
         "```",
         "cd /tmp && export TMPDIR=/tmp",
-        "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch -o run -- "
+        "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_fetch -o run -- "
         "python3 $REPO/bench.py --traffic-probe",
-        "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write -o run -- "
+        "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_write -o run -- "
         "python3 $REPO/bench.py --traffic-probe",
-        "python3 bench.py --traffic-parse gpurun_out/pmc_fetch/run_results.db gpurun_out/pmc_write/run_results.db",
+        "python3 bench.py --traffic-parse $OUT/pmc_fetch/run_results.db $OUT/pmc_write/run_results.db",
         "```", "",
         f"Each counter is scaled by bytes / counter for a plain {COPY_BYTES >> 20} MiB device copy "
         "(torch copy_: the same bytes read and written), medians over three dispatches.", "",
@@ -308,7 +308,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs the NVFP4 path on exactly one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported: there is no multi-GPU path in this build.",
+              f"(WORLD_SIZE={world}) is not supported: the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 

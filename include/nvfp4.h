@@ -58,7 +58,7 @@ extern "C" {
 #define NVFP4_ERR_NULL_ARG 1    /* a required pointer is NULL */
 #define NVFP4_ERR_SHAPE 2       /* negative dimension, K/cols not a multiple of 16, ... */
 #define NVFP4_ERR_ALIGN 3       /* a tensor pointer is not 16-byte aligned */
-#define NVFP4_ERR_UNSUPPORTED 4 /* valid NVFP4 problem outside this build's kernels */
+#define NVFP4_ERR_UNSUPPORTED 4 /* valid NVFP4 problem outside the kernels provided */
 #define NVFP4_ERR_WORKSPACE 5   /* workspace NULL or smaller than the query says */
 #define NVFP4_ERR_HIP 6         /* a HIP launch failed; see nvfp4_last_error() */
 

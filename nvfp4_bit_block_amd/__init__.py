@@ -58,8 +58,7 @@ def lib() -> ctypes.CDLL:
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(python -m nvfp4_bit_block_amd.build)")
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m nvfp4_bit_block_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, SZ, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
         sigs = {
