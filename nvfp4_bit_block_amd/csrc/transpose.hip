@@ -101,13 +101,15 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
 }
 
 // --------------------------------------------------- dequantize transpose --
-// Tile: 64 rows x 128 columns of the rowwise tensor (-> 128 rows x 64 columns
-// of y^T).  Decode: thread t owns the row pair 2 (t % 32), +1 and the
-// 16-column block t / 32; it decodes both rows' blocks and writes 16 words
-// (one output row each: the two rows' values at one column) into the
-// transposed LDS tile.  Store: 16 bytes (8 values) per thread, 8 threads per
-// output row.
-constexpr int kDR = 64, kDC = 128;
+// Tile: 128 rows x 128 columns of the rowwise tensor (-> 128 x 128 of y^T).
+// Decode: thread t owns the row pair 2 (t / 4), +1 and the 32-column quarter
+// t % 4 (16 code bytes of each row, so a load instruction of a wave covers 16
+// rows x 64 bytes); it decodes both rows' two blocks and writes 32 words (one
+// output row each: the two rows' values at one column) into the transposed
+// LDS tile.  Word w of output row c sits at w ^ (16 * (c / 32)), which puts
+// the 64 lanes of a wave's LDS writes on 64 different banks.  Store: 16 bytes
+// (8 values) per thread, 16 threads per 256-byte output row.
+constexpr int kDR = 128, kDC = 128;
 constexpr int kDStride = kDR / 2 + 1;  // words per LDS row of y^T
 
 __device__ __forceinline__ void dequant16(uint2 c, float s, float Sg, uint32_t out[8]) {
@@ -132,31 +134,44 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint8_t* __restric
     __shared__ uint32_t tile[kDC * kDStride];
     const float Sg = *sg_ptr;
     const int64_t r0 = (int64_t)blockIdx.y * kDR, c0 = (int64_t)blockIdx.x * kDC;
-    const int rp = threadIdx.x & 31, blk = threadIdx.x >> 5;
-    const int64_t r = r0 + 2 * rp, cb = c0 + 16 * blk;
-    uint32_t v0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, v1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (cb < C) {
-        const int64_t bpr = C / 16;
-        if (r < R)
-            dequant16(*reinterpret_cast<const uint2*>(codes + r * (C / 2) + cb / 2),
-                      e4m3_to_f32(scales[r * bpr + cb / 16]), Sg, v0);
-        if (r + 1 < R)
-            dequant16(*reinterpret_cast<const uint2*>(codes + (r + 1) * (C / 2) + cb / 2),
-                      e4m3_to_f32(scales[(r + 1) * bpr + cb / 16]), Sg, v1);
-    }
-    // y^T row 16 blk + i, word rp = (row r value, row r + 1 value) at column cb + i
+    const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
+    const int64_t r = r0 + 2 * p, cq = c0 + 32 * q;
+    const int64_t bpr = C / 16;
+    uint32_t v[2][2][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        tile[(16 * blk + 2 * i) * kDStride + rp] = (v0[i] & 0xFFFFu) | (v1[i] << 16);
-        tile[(16 * blk + 2 * i + 1) * kDStride + rp] = (v0[i] >> 16) | (v1[i] & 0xFFFF0000u);
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[a][b][i] = 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int64_t row = r + a;
+        if (row >= R) continue;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t c = cq + 16 * b;   // C % 16 == 0: a block is whole or absent
+            if (c + 16 > C) continue;
+            dequant16(*reinterpret_cast<const uint2*>(codes + row * (C / 2) + c / 2),
+                      e4m3_to_f32(scales[row * bpr + c / 16]), Sg, v[a][b]);
+        }
     }
+    const int swz = q << 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int col = 32 * q + 16 * b + 2 * i;
+            tile[col * kDStride + (p ^ swz)] = (v[0][b][i] & 0xFFFFu) | (v[1][b][i] << 16);
+            tile[(col + 1) * kDStride + (p ^ swz)] = (v[0][b][i] >> 16) | (v[1][b][i] & 0xFFFF0000u);
+        }
     __syncthreads();
 #pragma unroll
-    for (int pass = 0; pass < kDC / 32; ++pass) {
-        const int lrow = pass * 32 + (threadIdx.x >> 3), lw = (threadIdx.x & 7) * 4;
+    for (int pass = 0; pass < kDC / 16; ++pass) {
+        const int lrow = pass * 16 + (threadIdx.x >> 4), lw = (threadIdx.x & 15) * 4;
         const int64_t orow = c0 + lrow, ocol = r0 + 2 * lw;   // y^T [C, R]
         if (orow >= C || ocol >= R) continue;                // R % 8 == 0: whole 8-value pieces
-        const uint32_t* src = tile + lrow * kDStride + lw;
+        const uint32_t* src = tile + lrow * kDStride + (lw ^ ((lrow >> 5) << 4));
         const u32x4 w = {src[0], src[1], src[2], src[3]};
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(y_t + orow * R + ocol));
     }
