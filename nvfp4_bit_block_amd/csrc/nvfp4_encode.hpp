@@ -21,21 +21,23 @@ __device__ __forceinline__ uint32_t encode_elem(uint32_t h, float d) {
     return ((h >> 12) & 8u) | e2m1_from_f32(v);
 }
 
-// Correctly rounded fp32 quotient a / d without a divide instruction, for
-// |a| <= 8 d, d in [2^-100, 2^125) and y = RN(1 / d): q0 = a * y is within a
-// few ulps; each fma gives the remainder q * d - a exactly, and two
-// Newton-Markstein corrections q - (q * d - a) * y land on RN(a / d).  The
-// bounds keep y, the quotient and every remainder clear of overflow and of
-// the subnormal range where the remainder stops being exact.  The remainder
-// is formed as q * d - a (not a - q * d) so that a zero a keeps its sign
-// through both corrections.
-__device__ __forceinline__ float div_rn(float a, float d, float y) {
+// The fp32 quotient a / d for the E2M1 rounding decision, without a divide
+// instruction, for bf16 a with |a| <= 8 d, d in [2^-100, 2^125) and
+// y = RN(1 / d): q0 = a * y is within a few ulps, the fma gives the remainder
+// q0 * d - a exactly, and one Newton-Markstein correction
+// q0 - (q0 * d - a) * y is faithful (within one ulp of a / d, same sign).  A
+// one-ulp difference from RN(a / d) can change the E2M1 code only next to a
+// midpoint of the E2M1 grid, and there the corrected quotient equals
+// RN(a / d): the codes are those of the IEEE quotient (checked on the host
+// for every bf16 numerator).  The bounds keep y, the quotient and the
+// remainder clear of overflow and of the subnormal range where the remainder
+// stops being exact; the remainder is formed as q0 * d - a so that a zero a
+// keeps its sign.
+__device__ __forceinline__ float div_e2m1(float a, float d, float y) {
 #pragma clang fp contract(off)
     const float q0 = a * y;
     const float n0 = __builtin_fmaf(q0, d, -a);
-    const float q1 = __builtin_fmaf(-n0, y, q0);
-    const float n1 = __builtin_fmaf(q1, d, -a);
-    return __builtin_fmaf(-n1, y, q1);
+    return __builtin_fmaf(-n0, y, q0);
 }
 
 // Two bf16 elements (one 32-bit word) -> their E2M1 codes in byte SEL of acc.
@@ -45,8 +47,8 @@ __device__ __forceinline__ float div_rn(float a, float d, float y) {
 template <int SEL>
 __device__ __forceinline__ uint32_t encode_pair(uint32_t acc, uint32_t w, float d, float y) {
 #pragma clang fp contract(off)
-    const float ql = div_rn(__uint_as_float(w << 16), d, y);
-    const float qh = div_rn(__uint_as_float(w & 0xFFFF0000u), d, y);
+    const float ql = div_e2m1(__uint_as_float(w << 16), d, y);
+    const float qh = div_e2m1(__uint_as_float(w & 0xFFFF0000u), d, y);
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, ql, qh, 1.0f, SEL);
 }
 
@@ -61,7 +63,7 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t w[8], float Sg, 
     const float s_f = (t > 0.0f) ? bmax / t : 0.0f;
     const uint32_t s8 = e4m3_from_f32(s_f);
     const float d = e4m3_to_f32(s8) * Sg;
-    // Fast path when the exact-quotient conditions hold for every element
+    // Fast path when the quotient conditions hold for every element
     // (|x| <= bmax <= 8 d): all blocks of ordinary tensors.  Saturated scales,
     // zero blocks and extreme global scales take the IEEE division.
     if (d >= 0x1p-100f && d < 0x1p125f && bmax <= 8.0f * d) {
