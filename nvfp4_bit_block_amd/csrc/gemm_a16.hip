@@ -16,11 +16,14 @@
 // activation arrives already decoded (its quantizer writes q * s directly)
 // and only the weight tile is decoded here, once per wave that uses it.
 //
-// Data movement, per 64-wide K step (double-buffered in LDS, one barrier per
-// step): the workgroup loads the A tile (BM rows x 128 bytes, 8 lanes per
-// row) and the packed B tile (BN rows x 32 code bytes + 4 scale bytes)
-// through registers into LDS.  Waves read A fragments and packed B fragments
-// from LDS, decode B in registers and issue the MFMAs.
+// Data movement, per 64-wide K step: the A tile (BM rows x 128 bytes) and the
+// packed B tile (BN rows x 32 code bytes + 4 scale bytes) go from global
+// memory straight into LDS (buffer_load ... lds: each load instruction of a
+// wave fills 1 KB of LDS, 16 bytes per lane in lane order, or 256 bytes with
+// 4-byte loads), into one of NS stage buffers, so that NS - 1 steps are in
+// flight while a step is multiplied; one barrier per step.  Waves read A
+// fragments and packed B fragments from LDS, decode B in registers and issue
+// the MFMAs.
 //
 // K order inside a step: the 32x32x16 MFMA takes, in lane l, row (or column)
 // l % 32 and 8 consecutive K positions selected by l / 32.  A K permutation
@@ -29,8 +32,10 @@
 // uses positions 32 hf + 8 kk + [0, 8): a lane's packed B share is 16
 // contiguous code bytes and two scale bytes.
 //
-// LDS rows are padded (A: 144 bytes, B codes: 48 bytes) so that the 16-byte
-// reads of 16 consecutive rows fall on distinct banks.
+// LDS rows are not padded (the copy fixes the layout); instead the 16-byte
+// chunks of a row are permuted so that the 16-byte fragment reads of 16
+// consecutive rows fall on distinct banks: A row r keeps its chunk c in slot
+// c ^ ((r / 2) % 8), B column n its code half h in slot h ^ ((n / 8) % 2).
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
 
@@ -38,21 +43,41 @@ namespace nvfp4 {
 
 namespace {
 
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
-constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer built here
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data, range checked
+constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer built here
 
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+// Buffer resource over [base, base + bytes), in scalar registers.  Loads past
+// the end return zeros without a memory access.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
     const uint32_t n = bytes < 0x80000000ull ? (uint32_t)bytes : 0x80000000u;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+    r.z = __builtin_amdgcn_readfirstlane(n);
+    r.w = kRsrcWord3;
+    return r;
 }
-__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
+// Global -> LDS loads: lane l of the wave writes its 16 (or 4) bytes at LDS
+// byte address lds + 16 l (4 l); lds is wave-uniform and travels in M0 (one
+// wait state after the M0 write is required before the load).  Written as
+// asm so that the compiler does not make every later LDS read wait for them:
+// the K loop waits for them itself (vmcnt) before its barrier.  They have no
+// register results.
+__device__ __forceinline__ void lds_load16(u32x4 r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ uint32_t bload4(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+__device__ __forceinline__ void lds_load4(u32x4 r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
 }
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+// s_waitcnt immediate (gfx9) that waits until at most n vector memory
+// operations are outstanding, leaving the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -84,39 +109,44 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int kk) {
     return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
 }
 
-constexpr int kRowA = 144;   // LDS bytes per A row per step (128 + 16 of padding)
-constexpr int kRowB = 48;    // LDS bytes per B row of codes per step (32 + 16 of padding)
 constexpr int kGroupM = 8;   // m-tiles per band in the ungrouped tile order
 
-template <int TM, int TN, int WM, int WN>
+// Tile geometry and the per-step copy.  The copy is cut into 1 KB slabs, one
+// per 16-byte load instruction of a wave: 8 rows of A (128 bytes each), 32
+// columns of B codes (32 bytes each); the scales take one 4-byte load per
+// 64 columns.  Every wave issues the same number of loads per step (waves
+// without a B or scale slab load past the end of the buffer, which writes
+// zeros to an unused slab), so that the vmcnt waits are exact.
+template <int TM, int TN, int WM, int WN, int NS>
 struct Cfg {
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int WTM = 32 * TM, WTN = 32 * TN;
     static constexpr int BM = WTM * WM, BN = WTN * WN;
-    static constexpr int A_BYTES = BM * kRowA, BC_BYTES = BN * kRowB, BS_BYTES = BN * 4;
-    static constexpr int STAGE = A_BYTES + BC_BYTES + BS_BYTES;
-    // per-thread share of one step's copy
-    static constexpr int A_CHUNKS = BM * 8;                // 16-byte chunks of A
-    static constexpr int A_PER_T = A_CHUNKS / NT;
-    static constexpr int B_CHUNKS = BN * 2;                // 16-byte chunks of B codes
-    static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
-    static_assert(A_CHUNKS % NT == 0, "A copy");
-    static_assert(BN <= NT, "one scale word per thread");
-    static_assert(2 * STAGE <= 160 * 1024, "LDS");
+    static constexpr int A_SLABS = BM / 8, A_PER_W = A_SLABS / NW;
+    static constexpr int B_SLABS = BN / 32, B_PER_W = (B_SLABS + NW - 1) / NW;
+    static constexpr int S_SLABS = BN / 64;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = NW * B_PER_W * 1024, S_BYTES = NW * 256;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int LOADS = A_PER_W + B_PER_W + 1;   // load instructions per wave per step
+    static_assert(A_SLABS % NW == 0, "A copy");
+    static_assert(S_SLABS <= NW, "one scale load per wave");
+    static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+    static_assert(LOADS * (NS - 2) <= 63, "vmcnt");
 };
 
-// WPE: minimum waves per SIMD the register allocation must allow (1: no
-// constraint beyond the workgroup size).
-template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP, int WPE>
+// NS: LDS stage buffers (NS - 1 steps in flight).  WPE: minimum waves per
+// SIMD the register allocation must allow (1: no constraint beyond the
+// workgroup size).
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_gemm_a16(GemmArgs g) {
-    using C = Cfg<TM, TN, WM, WN>;
+    using C = Cfg<TM, TN, WM, WN, NS>;
     using Op = typename OpOf<AF>::T;
     constexpr int BM = C::BM, BN = C::BN, WTM = C::WTM, WTN = C::WTN;
     constexpr bool kGateUp = EP == Epi::kMoeGateUp || EP == Epi::kMoeGateUpLora;
     constexpr bool kLora = EP == Epi::kMoeGateUpLora || EP == Epi::kMoeDownLora;
     static_assert(!kGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
-    __shared__ __align__(16) uint8_t smem[2 * C::STAGE];
+    __shared__ __align__(1024) uint8_t smem[NS * C::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,9 +228,9 @@ void k_gemm_a16(GemmArgs g) {
     const uint32_t KB = (uint32_t)(g.K / 2), KS = (uint32_t)(g.K / 16), KA = (uint32_t)(g.K * 2);
     // A: 16-bit rows, optionally gathered, one resource over the source tensor
     // (the host keeps it below 2 GiB)
-    const Rsrc ra = make_rsrc(g.a, (uint64_t)g.a_src_rows * KA);
-    const Rsrc rb_c = make_rsrc(g.b_codes + (int64_t)grp * g.N * KB, (uint64_t)g.N * KB);
-    const Rsrc rb_s = make_rsrc(g.b_scales + (int64_t)grp * g.N * KS, (uint64_t)g.N * KS);
+    const u32x4 ra = make_rsrc(g.a, (uint64_t)g.a_src_rows * KA);
+    const u32x4 rb_c = make_rsrc(g.b_codes + (int64_t)grp * g.N * KB, (uint64_t)g.N * KB);
+    const u32x4 rb_s = make_rsrc(g.b_scales + (int64_t)grp * g.N * KS, (uint64_t)g.N * KS);
 
     // Global column of tile column n (or -1 past the end).
     auto b_col = [&](int n) -> int64_t {
@@ -282,16 +312,14 @@ void k_gemm_a16(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] *= lora_mul;
     }
-    // ---- this thread's copy assignments (fixed for the whole K loop)
-    // A: chunk p = tid + NT * u -> row p / 8, 16-byte chunk p % 8 of the row's step
-    // LDS offsets are one per-thread base plus compile-time steps, so that
-    // they cost one register each and the steps go into the instructions'
-    // offset fields.
-    uint32_t va[C::A_PER_T];
-    const uint32_t la0 = (uint32_t)((tid >> 3) * kRowA + 16 * (tid & 7));
+    // ---- this lane's copy assignments (fixed for the whole K loop)
+    // A slab sl = A_PER_W wave + u: rows 8 sl + lane / 8, LDS slot lane % 8,
+    // which receives the row's 16-byte chunk slot ^ ((row / 2) % 8).
+    uint32_t va[C::A_PER_W];
 #pragma unroll
-    for (int u = 0; u < C::A_PER_T; ++u) {
-        const int p = tid + C::NT * u, r = p >> 3, cc = p & 7;
+    for (int u = 0; u < C::A_PER_W; ++u) {
+        const int r = 8 * (C::A_PER_W * wave + u) + (lane >> 3);
+        const int cc = (lane & 7) ^ ((r >> 1) & 7);
         const int64_t row = row_beg + r;
         uint32_t v = kOob;
         if (row < row_end) {
@@ -300,70 +328,64 @@ void k_gemm_a16(GemmArgs g) {
         }
         va[u] = v;
     }
-    // B codes: chunk p = tid + NT * u (p < 2 BN) -> column p / 2, half p % 2
-    uint32_t vbc[C::B_PER_T], lbc[C::B_PER_T];
+    // B code slab sb = B_PER_W wave + u: columns 32 sb + lane / 2, LDS half
+    // lane % 2, which receives the column's code half (lane % 2) ^ ((n / 8) % 2).
+    uint32_t vbc[C::B_PER_W];
 #pragma unroll
-    for (int u = 0; u < C::B_PER_T; ++u) {
-        const int p = tid + C::NT * u;
-        const int n = p >> 1, h2 = p & 1;
+    for (int u = 0; u < C::B_PER_W; ++u) {
+        const int sb = C::B_PER_W * wave + u;
+        const int n = 32 * sb + (lane >> 1);
+        const int h2 = (lane & 1) ^ ((n >> 3) & 1);
         uint32_t v = kOob;
-        if (p < C::B_CHUNKS) {
+        if (sb < C::B_SLABS) {
             const int64_t col = b_col(n);
             if (col >= 0) v = (uint32_t)col * KB + 16u * h2;
         }
         vbc[u] = v;
-        lbc[u] = C::A_BYTES + (p < C::B_CHUNKS ? n * kRowB + 16 * h2 : 0);
     }
-    // B scales: thread tid < BN copies column tid's 4 scale bytes of the step
+    // B scales: wave w < S_SLABS loads the step's 4 scale bytes of columns 64 w + lane
     uint32_t vbs = kOob;
-    if (tid < BN) {
-        const int64_t col = b_col(tid);
+    if (wave < C::S_SLABS) {
+        const int64_t col = b_col(64 * wave + lane);
         if (col >= 0) vbs = (uint32_t)col * KS;
     }
-    const uint32_t lbs = C::A_BYTES + C::BC_BYTES + 4 * (tid < BN ? tid : 0);
-
-    // PD register sets, each holding one step's share of the copy: step t
-    // lives in set t % PD, so the loads of PD steps are in flight at once.
-    struct StageRegs {
-        uint4 a[C::A_PER_T], b[C::B_PER_T];
-        uint32_t s;
-    };
-    StageRegs stg[PD];
-    auto load_step = [&](StageRegs& r, int kc) {
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+    // Step kc of this workgroup's K range into stage buffer st.
+    auto issue = [&](int kc, int st) {
+        const uint32_t b = lds0 + (uint32_t)(st * C::STAGE);
 #pragma unroll
-        for (int u = 0; u < C::A_PER_T; ++u) r.a[u] = bload16(ra, va[u], (uint32_t)kc * 128u);
+        for (int u = 0; u < C::A_PER_W; ++u)
+            lds_load16(ra, va[u], (uint32_t)kc * 128u, b + (uint32_t)((C::A_PER_W * wave + u) * 1024));
 #pragma unroll
-        for (int u = 0; u < C::B_PER_T; ++u) r.b[u] = bload16(rb_c, vbc[u], (uint32_t)kc * 32u);
-        r.s = bload4(rb_s, vbs, (uint32_t)kc * 4u);
-    };
-    auto store_step = [&](const StageRegs& r, int buf) {
-        uint8_t* base = smem + buf * C::STAGE;
-#pragma unroll
-        for (int u = 0; u < C::A_PER_T; ++u) *reinterpret_cast<uint4*>(base + la0 + u * (C::NT / 8) * kRowA) = r.a[u];
-#pragma unroll
-        for (int u = 0; u < C::B_PER_T; ++u)
-            if (tid + C::NT * u < C::B_CHUNKS) *reinterpret_cast<uint4*>(base + lbc[u]) = r.b[u];
-        if (tid < BN) *reinterpret_cast<uint32_t*>(base + lbs) = r.s;
+        for (int u = 0; u < C::B_PER_W; ++u)
+            lds_load16(rb_c, vbc[u], (uint32_t)kc * 32u, b + (uint32_t)(C::A_BYTES + (C::B_PER_W * wave + u) * 1024));
+        lds_load4(rb_s, vbs, (uint32_t)kc * 4u, b + (uint32_t)(C::A_BYTES + C::B_BYTES + 256 * wave));
     };
 
-    // ---- fragment addresses within a stage buffer
-    const uint32_t fa0 = (uint32_t)((wm * WTM + c32) * kRowA + 64 * hf);
-    const uint32_t fbc0 = (uint32_t)(C::A_BYTES + (wn * WTN + c32) * kRowB + 16 * hf);
-    const uint32_t fbs0 = (uint32_t)(C::A_BYTES + C::BC_BYTES + 4 * (wn * WTN + c32));
-    auto fa = [&](int i) { return fa0 + 32 * i * kRowA; };
-    auto fbc = [&](int j) { return fbc0 + 32 * j * kRowB; };
+    // ---- fragment addresses within a stage buffer.  A: row wm WTM + 32 i +
+    // c32, chunk 4 hf + kk, in slot (4 hf + kk) ^ ((c32 / 2) % 8) (the row's
+    // other terms are multiples of 32); B: column wn WTN + 32 j + c32, code
+    // half hf in slot hf ^ ((c32 / 8) % 2); scales: 4 bytes per column.
+    uint32_t fa_k[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        fa_k[kk] = (uint32_t)((wm * WTM + c32) * 128 + 16 * ((4 * hf + kk) ^ ((c32 >> 1) & 7)));
+    const uint32_t fbc0 = (uint32_t)(C::A_BYTES + (wn * WTN + c32) * 32 + 16 * (hf ^ ((c32 >> 3) & 1)));
+    const uint32_t fbs0 = (uint32_t)(C::A_BYTES + C::B_BYTES + 4 * (wn * WTN + c32));
+    auto fa = [&](int i, int kk) { return fa_k[kk] + 32 * 128 * i; };
+    auto fbc = [&](int j) { return fbc0 + 32 * 32 * j; };
     auto fbs = [&](int j) { return fbs0 + 128 * j; };
 
-    // One K step from LDS buffer `buf`: the A fragments of MFMA group kk + 1
+    // One K step from stage buffer `st`: the A fragments of MFMA group kk + 1
     // are requested before the MFMAs of group kk are issued (the scheduling
     // barriers keep that order; left alone, the scheduler re-reads fragments
     // just in time to save registers and the MFMAs wait on LDS latency).
     // Waves whose rows all lie past the end of the row tile (a group's last,
     // partly filled tile) skip their MFMAs; the copy work stays shared.
     const bool wave_rows = (int64_t)wm * WTM < row_end - row_beg;
-    auto compute_step = [&](int buf) {
+    auto compute_step = [&](int st) {
         if (!wave_rows) return;
-        const uint8_t* base = smem + buf * C::STAGE;
+        const uint8_t* base = smem + st * C::STAGE;
         uint4 cb[TN];
         f32x2 sb[TN];
 #pragma unroll
@@ -373,13 +395,13 @@ void k_gemm_a16(GemmArgs g) {
         }
         Op av[2][TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) av[0][i] = *reinterpret_cast<const Op*>(base + fa(i));
+        for (int i = 0; i < TM; ++i) av[0][i] = *reinterpret_cast<const Op*>(base + fa(i, 0));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (kk + 1 < 4) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    av[(kk + 1) & 1][i] = *reinterpret_cast<const Op*>(base + fa(i) + 16 * (kk + 1));
+                    av[(kk + 1) & 1][i] = *reinterpret_cast<const Op*>(base + fa(i, kk + 1));
             }
             Op bv[TN];
 #pragma unroll
@@ -394,35 +416,37 @@ void k_gemm_a16(GemmArgs g) {
         }
     };
 
-    // ---- main loop, one barrier per step: iteration s multiplies LDS buffer
-    // s % 2, then writes step s + 1 from its register set into the other
-    // buffer (last read in iteration s - 1, before the previous barrier) and
-    // refills that set with step s + 1 + PD.  Loads past the last step re-read
-    // it (the clamp keeps the load count per iteration fixed, so the waits
-    // stay exact); their data is never multiplied.
+    // ---- main loop, one barrier per step.  Iteration s issues step
+    // s + NS - 1 into stage (s + NS - 1) % NS (multiplied in iteration s - 1,
+    // before the previous barrier), multiplies stage s % NS, then waits until
+    // step s + 1 has landed (only the loads of steps s + 2 .. s + NS - 1 may
+    // remain) and meets the barrier.  Loads past the last step re-read it, so
+    // every iteration issues C::LOADS loads per wave and the waits stay
+    // exact; their data is never multiplied.
+    constexpr int kWaitNext = vmcnt_imm(C::LOADS * (NS - 2));
     if (nsteps > 0) {
 #pragma unroll
-        for (int u = 0; u < PD; ++u) load_step(stg[u], kc0 + min(u, nsteps - 1));
-        store_step(stg[0], 0);
-        load_step(stg[0], kc0 + min(PD, nsteps - 1));
+        for (int u = 0; u + 1 < NS; ++u) issue(kc0 + min(u, nsteps - 1), u);
+        __builtin_amdgcn_s_waitcnt(kWaitNext);
         __syncthreads();
     }
-    auto step = [&](int s, StageRegs& next) {
-        compute_step(s & 1);
-        store_step(next, (s + 1) & 1);
-        load_step(next, kc0 + min(s + 1 + PD, nsteps - 1));
+    auto step = [&](int s, int st) {
+        issue(kc0 + min(s + NS - 1, nsteps - 1), (st + NS - 1) % NS);
+        compute_step(st);
+        __builtin_amdgcn_s_waitcnt(kWaitNext);
         __syncthreads();
     };
-    // whole groups of PD steps without conditions (exact wait counts), then
+    // whole groups of NS steps (stage numbers known at compile time), then
     // the remaining steps
-    const int nmain = nsteps / PD * PD;
-    for (int s0 = 0; s0 < nmain; s0 += PD) {
+    const int nmain = nsteps / NS * NS;
+    for (int s0 = 0; s0 < nmain; s0 += NS) {
 #pragma unroll
-        for (int u = 0; u < PD; ++u) step(s0 + u, stg[(u + 1) % PD]);
+        for (int u = 0; u < NS; ++u) step(s0 + u, u);
     }
 #pragma unroll
-    for (int u = 0; u < PD; ++u)
-        if (nmain + u < nsteps) step(nmain + u, stg[(u + 1) % PD]);
+    for (int u = 0; u + 1 < NS; ++u)
+        if (nmain + u < nsteps) step(nmain + u, u);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32
 #pragma unroll
@@ -460,9 +484,9 @@ void k_gemm_a16(GemmArgs g) {
     }
 }
 
-template <int TM, int TN, int WM, int WN, int PD, AFmt AF, Epi EP, int WPE = 1>
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1>
 hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
-    using C = Cfg<TM, TN, WM, WN>;
+    using C = Cfg<TM, TN, WM, WN, NS>;
     GemmArgs g = g0;
     int64_t wgs;
     if (g.groups > 0) {
@@ -476,22 +500,22 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     } else {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, PD, AF, EP, WPE>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
 }
 
 template <AFmt AF, Epi EP>
 hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t stream) {
     switch (tile) {
-        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, 1, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 1, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 1, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP, 3>(g, grid_m, stream);
-        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
-        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 4, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 5, AF, EP>(g, grid_m, stream);
+        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 5, AF, EP>(g, grid_m, stream);
     }
     return hipErrorInvalidValue;
 }
