@@ -514,8 +514,8 @@ hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t 
         case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP, 3>(g, grid_m, stream);
         case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
-        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 5, AF, EP>(g, grid_m, stream);
-        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 5, AF, EP>(g, grid_m, stream);
+        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
     }
     return hipErrorInvalidValue;
 }
