@@ -383,6 +383,10 @@ void k_gemm_a16(GemmArgs g) {
     // Waves whose rows all lie past the end of the row tile (a group's last,
     // partly filled tile) skip their MFMAs; the copy work stays shared.
     const bool wave_rows = (int64_t)wm * WTM < row_end - row_beg;
+    // Grouped tiles: a wave whose rows past the first 32 are all padding
+    // skips the MFMAs of its second 32-row block.
+    constexpr bool kHalfSkip = TM == 2 && EP != Epi::kStoreBf16 && EP != Epi::kPartialF32;
+    const bool wave_half = kHalfSkip && (int64_t)wm * WTM + 32 >= row_end - row_beg;
     auto compute_step = [&](int st) {
         if (!wave_rows) return;
         const uint8_t* base = smem + st * C::STAGE;
@@ -409,9 +413,11 @@ void k_gemm_a16(GemmArgs g) {
                 bv[j] = decode_w(word(cb[j], kk), kk < 2 ? sb[j].x : sb[j].y, (Op*)nullptr);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
+                if (i > 0 && wave_half) break;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma(av[kk & 1][i], bv[j], acc[i][j]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
