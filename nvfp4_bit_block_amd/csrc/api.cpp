@@ -70,11 +70,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         return M <= 64 ? tiles * p.ksplit * 2 <= 256 : tiles * p.ksplit < 256;
     };
     while (wants_split() && p.ksplit < 16 && ksteps / (p.ksplit * 2) >= 8) p.ksplit *= 2;
-    // 256-511 tiles of 128 x 128 on long K (o_proj at M = 1024: 384 tiles)
-    // leave some CUs one tile and others two; split 2 gives every CU three
-    // workgroups at once (W4A4 246.6 -> 234.2 us, W4A16 267.8 -> 242.1 us).
-    // Short K or the other tiles measured slower with any extra split.
-    if (p.tile == A16Tile::k128x128_w64x64 && p.ksplit == 1 && tiles >= 256 && tiles < 512 && ksteps >= 128)
+    // 256-511 tiles on long K leave some CUs one tile and others two (o_proj
+    // at M = 1024: 384 tiles of 128 x 128, three workgroups per CU; at
+    // M = 4096: 384 tiles of 256 x 256, one per CU, so 1.5 rounds); split 2
+    // evens the load (M = 1024: W4A4 246.6 -> 234.2 us, W4A16 267.8 -> 242.1;
+    // M = 4096: W4A4 814 -> 767 us, W4A16 861 -> 801).  Short K, more tiles
+    // or further splits measured slower: each split adds a partial-sum pass.
+    if ((p.tile == A16Tile::k128x128_w64x64 || p.tile == A16Tile::k256x256_w128x64) && p.ksplit == 1 &&
+        tiles >= 256 && tiles < 512 && ksteps >= 128)
         p.ksplit = 2;
     return p;
 }
