@@ -527,17 +527,64 @@ hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t 
 }
 
 // Split-K finish: y = bf16(scale * sum_s partial[s]) with the splits summed
-// in order.
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial, int ksplit,
-                                                       int64_t M, int64_t N, const float* __restrict__ g0,
-                                                       const float* __restrict__ g1, uint16_t* __restrict__ y) {
+// in order (s = 0 + p0 + p1 + ...).  KS is the split count, so that a thread
+// issues all KS loads before its first add; V = 4 outputs per thread with
+// 16-byte loads (M N % 4 == 0), else 1.
+template <int KS, int V>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial, int64_t total,
+                                                       const float* __restrict__ g0, const float* __restrict__ g1,
+                                                       uint16_t* __restrict__ y, bool y8) {
     const float scale = *g0 * (g1 ? *g1 : 1.0f);
-    const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        float s = 0.0f;
-        for (int k = 0; k < ksplit; ++k) s += partial[(int64_t)k * total + i];
-        y[i] = (uint16_t)f32_to_bf16_rne(s * scale);
+    const int64_t n = total / V;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) {
+        if constexpr (V == 4) {
+            f32x4 p[KS];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) p[k] = *reinterpret_cast<const f32x4*>(partial + k * total + 4 * v);
+            float s[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[e] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < KS; ++k) s[e] += p[k][e];
+            }
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(s[e] * scale);
+            if (y8) {
+                *reinterpret_cast<uint2*>(y + 4 * v) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[4 * v + e] = (uint16_t)b[e];
+            }
+        } else {
+            float p[KS];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) p[k] = partial[k * total + v];
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) s += p[k];
+            y[v] = (uint16_t)f32_to_bf16_rne(s * scale);
+        }
     }
+}
+
+template <int KS>
+hipError_t launch_reduce_ks(const float* partial, int64_t total, const float* g0, const float* g1, uint16_t* y,
+                            hipStream_t stream) {
+    const bool vec = (total % 4) == 0 && (reinterpret_cast<uintptr_t>(partial) & 15u) == 0;
+    const int64_t n = vec ? total / 4 : total;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 8192) grid = 8192;
+    if (grid < 1) grid = 1;
+    const bool y8 = (reinterpret_cast<uintptr_t>(y) & 7u) == 0;
+    if (vec)
+        hipLaunchKernelGGL((k_splitk_reduce<KS, 4>), dim3((unsigned)grid), dim3(256), 0, stream, partial, total, g0,
+                           g1, y, y8);
+    else
+        hipLaunchKernelGGL((k_splitk_reduce<KS, 1>), dim3((unsigned)grid), dim3(256), 0, stream, partial, total, g0,
+                           g1, y, y8);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -598,12 +645,14 @@ hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, 
 
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
-    int64_t grid = (M * N + 255) / 256;
-    if (grid > 8192) grid = 8192;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)grid), dim3(256), 0, stream, partial, ksplit, M, N, g0, g1,
-                       y);
-    return hipGetLastError();
+    const int64_t total = M * N;
+    switch (ksplit) {
+        case 2: return launch_reduce_ks<2>(partial, total, g0, g1, y, stream);
+        case 4: return launch_reduce_ks<4>(partial, total, g0, g1, y, stream);
+        case 8: return launch_reduce_ks<8>(partial, total, g0, g1, y, stream);
+        case 16: return launch_reduce_ks<16>(partial, total, g0, g1, y, stream);
+        default: return hipErrorInvalidValue;   // the split-K plan uses powers of two up to 16
+    }
 }
 
 }  // namespace nvfp4
