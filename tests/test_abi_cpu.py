@@ -119,7 +119,9 @@ def test_gemm_w4a16_validation():
     g = L.nvfp4_gemm_w4a16
     ws = L.nvfp4_gemm_w4a16_workspace_size(128, 256, 4096)
     assert ws > 0                                            # split K: partial sums
-    assert L.nvfp4_gemm_w4a16_workspace_size(4096, 6144, 16384) == 0
+    assert L.nvfp4_gemm_w4a16_workspace_size(4096, 16384, 2048) == 0   # 1024 tiles, no split
+    # o_proj at M = 4096: 384 tiles of 256 x 256, K split in two (two fp32 partials)
+    assert L.nvfp4_gemm_w4a16_workspace_size(4096, 6144, 16384) == 2 * 4096 * 6144 * 4
     assert g(None, 128, 256, 4096, A, A, A, A, A, ws, None) == NULL
     assert g(A, 128, 256, 4100, A, A, A, A, A, ws, None) == SHAPE
     assert g(A, 128, 256, 4128, A, A, A, A, A, 1 << 30, None) == UNSUP   # K % 64 != 0
