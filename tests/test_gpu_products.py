@@ -86,8 +86,11 @@ def test_gemm_tiny_end_to_end(orc):
     assert_close(host_bf16_f32(y), orc.gemm_w4a4(x, isc, c0, s0, g0), "gemm tiny")
 
 
+# (9, 201, 2048) and (13, 75, 4096) split K four and eight ways with M N odd,
+# which takes the split-K reduce's one-output-per-thread path
 @pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (8, 256, 512), (9, 200, 256), (37, 200, 256),
-                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640)])
+                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640),
+                                   (9, 201, 2048), (13, 75, 4096)])
 def test_gemm_shapes(orc, M, N, K):
     _gemm_case(orc, M, N, K, seed=M * 7 + N)
 
@@ -117,7 +120,7 @@ def _packed_matches(orc, x, isc, c, s, g, what):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (3, 200, 2048), (5, 67, 16384), (9, 200, 256), (37, 200, 256),
-                                   (130, 384, 512), (300, 136, 640)])
+                                   (130, 384, 512), (300, 136, 640), (13, 75, 4096)])
 def test_gemm_packed_shapes(orc, M, N, K):
     # quantize once (static), then the GEMM on codes and scales: the same bits
     # as the one-call W4A4 GEMM, and within tolerance of the oracle
@@ -140,7 +143,8 @@ def test_gemm_packed_layers(orc, name, M):
 # ------------------------------------------------------- W4A16 over any M --
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (6, 200, 8192), (9, 200, 256), (37, 200, 256),
-                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640)])
+                                   (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640),
+                                   (9, 201, 2048)])
 def test_gemm_w4a16_shapes(orc, M, N, K):
     w = wl.layer_weight((N, K), seed=M * 5 + N)
     x = wl.activations(M, K, seed=M + K)
