@@ -139,3 +139,34 @@ def test_moe_full_size_sampled_tokens(orc, full_moe, mode, adapter):
     kw = dict(a13=a13[used], a2=a2[used]) if mode == 1 else {}
     ref = orc.moe(f["x"][rows], ids_s, f["wts"][rows], *host, mode=mode, lora=lora, **kw)
     assert_close(host_bf16_f32(y)[rows], ref, f"moe full size mode={mode} lora={adapter}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_moe_lora_zero_weight_scale(orc, mode):
+    """Experts whose weight global scale is 0: the weight product vanishes and
+    the grouped GEMM runs no K step at all for their tiles (the adapter term
+    alone, scaled by lora_scale, reaches the epilogue)."""
+    T, E, k, H, I, r, scale = 64, 8, 2, 256, 128, 32, 1.5
+    print(f"moe lora zero weight scale mode={mode}", flush=True)
+    x, ids, wts, cw, gw = _moe_case(orc, T, E, k, H, I, seed=21)
+    zero = [1, 5]
+    for i in (2, 5):
+        cw[i] = cw[i].copy()
+        cw[i][zero] = 0.0
+        gw[i] = gw[i].clone()
+        gw[i][zero] = 0.0
+    lo = _lora(E, H, I, r, 22)
+    kw, gkw = {}, {}
+    if mode == 1:
+        _, h = orc.moe(x, ids, wts, *cw, mode=0, want_h=True, lora={"scale": scale, **lo})
+        a13 = np.full(E, orc.global_scale(x), np.float32)
+        a2 = np.full(E, orc.global_scale(h), np.float32)
+        kw = dict(a13=a13, a2=a2)
+        gkw = dict(a13_scale=dev(a13), a2_scale=dev(a2))
+    ref = orc.moe(x, ids, wts, *cw, mode=mode, lora={"scale": scale, **lo}, **kw)
+    y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=mode, lora=_dev_lora(lo, scale), **gkw)
+    torch.cuda.synchronize()
+    y = host_bf16_f32(y)
+    assert_close(y, ref, f"moe lora zero weight scale mode={mode}")
+    # tokens routed to a zeroed expert still get that expert's adapter output
+    assert np.isin(ids, zero).any() and np.abs(ref).max() > 0
