@@ -124,7 +124,8 @@ def traffic_parse(fetch_db, write_db):
 
 def counter_probe(kind):
     """Launch a plain 512 MiB copy three times, then the kernels of one row
-    three times, for a rocprofv3 --pmc pass (kind: quantize, gemm or moe)."""
+    three times, for a rocprofv3 --pmc pass (kind: quantize, gemm, gemm_small
+    or moe)."""
     import torch
     import nvfp4_bit_block_amd as nv
     import workloads as wl
@@ -144,6 +145,22 @@ def counter_probe(kind):
         xs = {}
         for name, K in (("q_b_proj", 2048), ("o_proj", 16384)):
             x = to_dev(wl.activations(4096, K, seed=4))
+            isc = torch.empty(1, dtype=torch.float32, device=dev)
+            nv.quantize(x, global_scale=isc)
+            xs[name] = (x, isc)
+
+        def run():
+            nv.gemm_w4a4(xs["q_b_proj"][0], xs["q_b_proj"][1], *wq)
+            nv.gemm_w4a4(xs["o_proj"][0], xs["o_proj"][1], *woq)
+    elif kind == "gemm_small":
+        # the weight-streaming regime: W4A4 at M = 32 on both layers
+        w, _ = wl.gemv_inputs("q_b_proj")
+        wq = nv.quantize(to_dev(w))
+        wo, _ = wl.gemv_inputs("o_proj")
+        woq = nv.quantize(to_dev(wo))
+        xs = {}
+        for name, K in (("q_b_proj", 2048), ("o_proj", 16384)):
+            x = to_dev(wl.activations(32, K, seed=4))
             isc = torch.empty(1, dtype=torch.float32, device=dev)
             nv.quantize(x, global_scale=isc)
             xs[name] = (x, isc)
@@ -256,7 +273,7 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch a plain 512 MiB copy and the batch-1 o_proj GEMV, three times each "
                          "(run this under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
-    ap.add_argument("--counter-probe", choices=("quantize", "gemm", "moe"),
+    ap.add_argument("--counter-probe", choices=("quantize", "gemm", "gemm_small", "moe"),
                     help="only launch a plain 512 MiB copy, then the quantize of 65536 x 6144, the W4A4 GEMM at "
                          "M = 4096 on q_b_proj and o_proj, or the MoE layer in both modes, three times each "
                          "(run under rocprofv3 --pmc)")
