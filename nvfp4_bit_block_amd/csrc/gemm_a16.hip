@@ -136,8 +136,10 @@ struct Cfg {
 
 // NS: LDS stage buffers (NS - 1 steps in flight).  WPE: minimum waves per
 // SIMD the register allocation must allow (1: no constraint beyond the
-// workgroup size).
-template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE>
+// workgroup size).  SJ: 16-byte scale chunks per column the workgroup may
+// preload (0: none; else the launcher guarantees at most 4 SJ K steps per
+// workgroup; see the preload below).
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE, int SJ = 0>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN, NS>;
@@ -146,7 +148,10 @@ void k_gemm_a16(GemmArgs g) {
     constexpr bool kGateUp = EP == Epi::kMoeGateUp || EP == Epi::kMoeGateUpLora;
     constexpr bool kLora = EP == Epi::kMoeGateUpLora || EP == Epi::kMoeDownLora;
     static_assert(!kGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
-    __shared__ __align__(1024) uint8_t smem[NS * C::STAGE];
+    constexpr int SP_OFF = NS * C::STAGE;
+    static_assert(SJ == 0 || (SJ <= 16 && (SJ & (SJ - 1)) == 0), "scale chunks");
+    static_assert(NS * C::STAGE + C::BN * SJ * 16 <= 160 * 1024, "LDS");
+    __shared__ __align__(1024) uint8_t smem[NS * C::STAGE + C::BN * SJ * 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -350,6 +355,13 @@ void k_gemm_a16(GemmArgs g) {
         if (col >= 0) vbs = (uint32_t)col * KS;
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+    // Scale preload (SJ > 0): a K step of a column has only 4 scale bytes, so
+    // a per-step scale load touches one cache line per 4 bytes.  Instead the
+    // workgroup's scales (at most 4 SJ steps) are loaded once, 16 bytes (four
+    // steps) per lane: column n keeps its chunk j in slot j ^ ((n / 2) % SJ)
+    // of SJ 16-byte slots.
+    constexpr bool sp = SJ > 0;
+    constexpr int sj = SJ;
     // Step kc of this workgroup's K range into stage buffer st.
     auto issue = [&](int kc, int st) {
         const uint32_t b = lds0 + (uint32_t)(st * C::STAGE);
@@ -359,7 +371,7 @@ void k_gemm_a16(GemmArgs g) {
 #pragma unroll
         for (int u = 0; u < C::B_PER_W; ++u)
             lds_load16(rb_c, vbc[u], (uint32_t)kc * 32u, b + (uint32_t)(C::A_BYTES + (C::B_PER_W * wave + u) * 1024));
-        lds_load4(rb_s, vbs, (uint32_t)kc * 4u, b + (uint32_t)(C::A_BYTES + C::B_BYTES + 256 * wave));
+        if constexpr (!sp) lds_load4(rb_s, vbs, (uint32_t)kc * 4u, b + (uint32_t)(C::A_BYTES + C::B_BYTES + 256 * wave));
     };
 
     // ---- fragment addresses within a stage buffer.  A: row wm WTM + 32 i +
@@ -387,7 +399,11 @@ void k_gemm_a16(GemmArgs g) {
     // skips the MFMAs of its second 32-row block.
     constexpr bool kHalfSkip = TM == 2 && EP != Epi::kStoreBf16 && EP != Epi::kPartialF32;
     const bool wave_half = kHalfSkip && (int64_t)wm * WTM + 32 >= row_end - row_beg;
-    auto compute_step = [&](int st) {
+    const int gsc = (c32 >> 1) & (sj > 0 ? sj - 1 : 0);
+    // (the tile's column offsets wn WTN + 32 j are multiples of 32, so the
+    // slot permutation of column wn WTN + 32 j + c32 depends on c32 alone)
+    const uint32_t fsp0 = (uint32_t)(SP_OFF + (wn * WTN + c32) * sj * 16);
+    auto compute_step = [&](int st, int ls) {
         if (!wave_rows) return;
         const uint8_t* base = smem + st * C::STAGE;
         uint4 cb[TN];
@@ -395,7 +411,9 @@ void k_gemm_a16(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             cb[j] = *reinterpret_cast<const uint4*>(base + fbc(j));
-            sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(base + fbs(j)) >> (16 * hf));
+            const uint8_t* sa = base + fbs(j);
+            if constexpr (sp) sa = smem + fsp0 + 32 * j * sj * 16 + 16 * ((ls >> 2) ^ gsc) + 4 * (ls & 3);
+            sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(sa) >> (16 * hf));
         }
         Op av[2][TM];
 #pragma unroll
@@ -429,17 +447,34 @@ void k_gemm_a16(GemmArgs g) {
     // remain) and meets the barrier.  Loads past the last step re-read it, so
     // every iteration issues C::LOADS loads per wave and the waits stay
     // exact; their data is never multiplied.
-    constexpr int kWaitNext = vmcnt_imm(C::LOADS * (NS - 2));
+    // (with the scale preload a step issues one load fewer per wave)
+    constexpr int kWaitNext = vmcnt_imm((sp ? C::LOADS - 1 : C::LOADS) * (NS - 2));
+    auto wait_next = [&]() { __builtin_amdgcn_s_waitcnt(kWaitNext); };
+    if constexpr (sp) {
+        if (nsteps > 0) {
+            // slot p = 64 u + lane holds column p / sj, chunk (p % sj) ^ ((n / 2) % sj);
+            // chunks past the K range read the next scales of the row (or zeros
+            // past the tensor) and are never used
+            constexpr int ni = C::BN * sj / 64;
+            for (int u = wave; u < ni; u += C::NW) {
+                const int p = 64 * u + lane, n = p / sj, j = (p % sj) ^ ((n >> 1) & (sj - 1));
+                const int64_t col = b_col(n);
+                const uint32_t v = col >= 0 ? (uint32_t)col * KS + (uint32_t)kc0 * 4u + 16u * j : kOob;
+                lds_load16(rb_s, v, 0u, lds0 + (uint32_t)(SP_OFF + 1024 * u));
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+    }
     if (nsteps > 0) {
 #pragma unroll
         for (int u = 0; u + 1 < NS; ++u) issue(kc0 + min(u, nsteps - 1), u);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        wait_next();
         __syncthreads();
     }
     auto step = [&](int s, int st) {
         issue(kc0 + min(s + NS - 1, nsteps - 1), (st + NS - 1) % NS);
-        compute_step(st);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        compute_step(st, s);
+        wait_next();
         __syncthreads();
     };
     // whole groups of NS steps (stage numbers known at compile time), then
@@ -490,7 +525,7 @@ void k_gemm_a16(GemmArgs g) {
     }
 }
 
-template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1>
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1, int SJ = 0>
 hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     using C = Cfg<TM, TN, WM, WN, NS>;
     GemmArgs g = g0;
@@ -506,8 +541,20 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     } else {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
+    if (SJ > 0 && ((g.K / 64) + g.ksplit - 1) / g.ksplit > 4 * SJ) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
+}
+
+// The small-M tiles preload their scales when a workgroup's K range is at
+// most 64 steps (16 chunks per column; 4 chunks up to 16 steps, which
+// over-reads less), else they load them per step.
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP>
+hipError_t launch_small(const GemmArgs& g, int grid_m, hipStream_t stream) {
+    const int64_t per = ((g.K / 64) + g.ksplit - 1) / g.ksplit;
+    if (per <= 16) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 4>(g, grid_m, stream);
+    if (per <= 64) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 16>(g, grid_m, stream);
+    return launch_cfg<TM, TN, WM, WN, NS, AF, EP>(g, grid_m, stream);
 }
 
 template <AFmt AF, Epi EP>
@@ -519,9 +566,9 @@ hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t 
         case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP, 3>(g, grid_m, stream);
-        case A16Tile::k128x128_w32x64: return launch_cfg<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
-        case A16Tile::k64x256_w64x64: return launch_cfg<2, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
-        case A16Tile::k32x256_w32x64: return launch_cfg<1, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k128x128_w32x64: return launch_small<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k64x256_w64x64: return launch_small<2, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k32x256_w32x64: return launch_small<1, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
     }
     return hipErrorInvalidValue;
 }
