@@ -547,12 +547,13 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
 }
 
 // The small-M tiles preload their scales when a workgroup's K range is at
-// most 64 steps (16 chunks per column; 4 chunks up to 16 steps, which
-// over-reads less), else they load them per step.
+// most 64 steps (4, 8 or 16 chunks per column, the fewest that cover it, so
+// that little is read past the range), else they load them per step.
 template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP>
 hipError_t launch_small(const GemmArgs& g, int grid_m, hipStream_t stream) {
     const int64_t per = ((g.K / 64) + g.ksplit - 1) / g.ksplit;
     if (per <= 16) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 4>(g, grid_m, stream);
+    if (per <= 32) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 8>(g, grid_m, stream);
     if (per <= 64) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 16>(g, grid_m, stream);
     return launch_cfg<TM, TN, WM, WN, NS, AF, EP>(g, grid_m, stream);
 }
