@@ -139,7 +139,7 @@ struct Cfg {
 // workgroup size).  SJ: 16-byte scale chunks per column the workgroup may
 // preload (0: none; else the launcher guarantees at most 4 SJ K steps per
 // workgroup; see the preload below).
-template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE, int SJ = 0>
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE, int SJ = 0, bool K2 = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN, NS>;
@@ -148,10 +148,15 @@ void k_gemm_a16(GemmArgs g) {
     constexpr bool kGateUp = EP == Epi::kMoeGateUp || EP == Epi::kMoeGateUpLora;
     constexpr bool kLora = EP == Epi::kMoeGateUpLora || EP == Epi::kMoeDownLora;
     static_assert(!kGateUp || (TN % 2) == 0, "gate/up needs paired column blocks");
-    constexpr int SP_OFF = NS * C::STAGE;
+    // K2: a stage holds two K steps: two A tiles, then the weight codes of
+    // both steps, 64 bytes per column (16-byte slot s of column n holding
+    // chunk s ^ ((n / 4) % 4)), loaded 16 columns per instruction
+    static_assert(!K2 || SJ > 0, "two-step stages need the scale preload");
+    constexpr int STG = K2 ? 2 * C::A_BYTES + C::BN * 64 : C::STAGE;
+    constexpr int SP_OFF = NS * STG;
     static_assert(SJ == 0 || (SJ <= 16 && (SJ & (SJ - 1)) == 0), "scale chunks");
-    static_assert(NS * C::STAGE + C::BN * SJ * 16 <= 160 * 1024, "LDS");
-    __shared__ __align__(1024) uint8_t smem[NS * C::STAGE + C::BN * SJ * 16];
+    static_assert(NS * STG + C::BN * SJ * 16 <= 160 * 1024, "LDS");
+    __shared__ __align__(1024) uint8_t smem[NS * STG + C::BN * SJ * 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,6 +368,32 @@ void k_gemm_a16(GemmArgs g) {
     constexpr bool sp = SJ > 0;
     constexpr int sj = SJ;
     // Step kc of this workgroup's K range into stage buffer st.
+    constexpr int B2_PER_W = C::BN / 16 / C::NW;
+    static_assert(!K2 || (C::BN / 16) % C::NW == 0, "two-step code slabs");
+    uint32_t vbc2[K2 ? B2_PER_W : 1];
+    if constexpr (K2) {
+#pragma unroll
+        for (int u = 0; u < B2_PER_W; ++u) {
+            const int n = 16 * (B2_PER_W * wave + u) + (lane >> 2);
+            const int c = (lane & 3) ^ ((n >> 2) & 3);
+            const int64_t col = b_col(n);
+            vbc2[u] = col >= 0 ? (uint32_t)col * KB + 16u * c : kOob;
+        }
+    }
+    // group kg (steps 2 kg, 2 kg + 1 of the range, clamped) into stage st
+    auto issue2 = [&](int kg, int st) {
+        const uint32_t b = lds0 + (uint32_t)(st * STG);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int kc = kc0 + min(2 * kg + g, nsteps - 1);
+#pragma unroll
+            for (int u = 0; u < C::A_PER_W; ++u)
+                lds_load16(ra, va[u], (uint32_t)kc * 128u, b + (uint32_t)(g * C::A_BYTES + (C::A_PER_W * wave + u) * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < B2_PER_W; ++u)
+            lds_load16(rb_c, vbc2[u], (uint32_t)(kc0 + 2 * kg) * 32u, b + (uint32_t)(2 * C::A_BYTES + (B2_PER_W * wave + u) * 1024));
+    };
     auto issue = [&](int kc, int st) {
         const uint32_t b = lds0 + (uint32_t)(st * C::STAGE);
 #pragma unroll
@@ -403,14 +434,13 @@ void k_gemm_a16(GemmArgs g) {
     // (the tile's column offsets wn WTN + 32 j are multiples of 32, so the
     // slot permutation of column wn WTN + 32 j + c32 depends on c32 alone)
     const uint32_t fsp0 = (uint32_t)(SP_OFF + (wn * WTN + c32) * sj * 16);
-    auto compute_step = [&](int st, int ls) {
+    auto compute_at = [&](const uint8_t* base, const uint8_t* cbase, int cstride, int ls) {
         if (!wave_rows) return;
-        const uint8_t* base = smem + st * C::STAGE;
         uint4 cb[TN];
         f32x2 sb[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            cb[j] = *reinterpret_cast<const uint4*>(base + fbc(j));
+            cb[j] = *reinterpret_cast<const uint4*>(cbase + cstride * j);
             const uint8_t* sa = base + fbs(j);
             if constexpr (sp) sa = smem + fsp0 + 32 * j * sj * 16 + 16 * ((ls >> 2) ^ gsc) + 4 * (ls & 3);
             sb[j] = e4m3x2_to_f32(*reinterpret_cast<const uint32_t*>(sa) >> (16 * hf));
@@ -439,6 +469,20 @@ void k_gemm_a16(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto compute_step = [&](int st, int ls) {
+        const uint8_t* base = smem + st * C::STAGE;
+        compute_at(base, base + fbc(0), 32 * 32, ls);
+    };
+    const uint32_t fbc2_0 = (uint32_t)(2 * C::A_BYTES + (wn * WTN + c32) * 64);
+    auto compute_group = [&](int st, int kg) {
+        const uint8_t* base = smem + st * STG;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int ls = 2 * kg + g;
+            if (ls < nsteps)
+                compute_at(base + g * C::A_BYTES, base + fbc2_0 + 16 * ((2 * g + hf) ^ ((c32 >> 2) & 3)), 32 * 64, ls);
+        }
+    };
 
     // ---- main loop, one barrier per step.  Iteration s issues step
     // s + NS - 1 into stage (s + NS - 1) % NS (multiplied in iteration s - 1,
@@ -464,6 +508,31 @@ void k_gemm_a16(GemmArgs g) {
             }
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
+    }
+    if constexpr (K2) {
+        constexpr int kWait2 = vmcnt_imm((2 * C::A_PER_W + B2_PER_W) * (NS - 2));
+        const int ngroups = (nsteps + 1) / 2;
+        if (nsteps > 0) {
+#pragma unroll
+            for (int u = 0; u + 1 < NS; ++u) issue2(min(u, ngroups - 1), u);
+            __builtin_amdgcn_s_waitcnt(kWait2);
+            __syncthreads();
+        }
+        auto gstep = [&](int s, int st) {
+            issue2(min(s + NS - 1, ngroups - 1), (st + NS - 1) % NS);
+            compute_group(st, s);
+            __builtin_amdgcn_s_waitcnt(kWait2);
+            __syncthreads();
+        };
+        const int gmain = ngroups / NS * NS;
+        for (int s0 = 0; s0 < gmain; s0 += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) gstep(s0 + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u + 1 < NS; ++u)
+            if (gmain + u < ngroups) gstep(gmain + u, u);
+        nsteps = 0;   // the single-step loop below has nothing left to do
     }
     if (nsteps > 0) {
 #pragma unroll
@@ -525,7 +594,7 @@ void k_gemm_a16(GemmArgs g) {
     }
 }
 
-template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1, int SJ = 0>
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1, int SJ = 0, bool K2 = false>
 hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     using C = Cfg<TM, TN, WM, WN, NS>;
     GemmArgs g = g0;
@@ -542,7 +611,7 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
     if (SJ > 0 && ((g.K / 64) + g.ksplit - 1) / g.ksplit > 4 * SJ) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ, K2>), dim3((unsigned)wgs), dim3(C::NT), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -552,9 +621,9 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
 template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP>
 hipError_t launch_small(const GemmArgs& g, int grid_m, hipStream_t stream) {
     const int64_t per = ((g.K / 64) + g.ksplit - 1) / g.ksplit;
-    if (per <= 16) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 4>(g, grid_m, stream);
-    if (per <= 32) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 8>(g, grid_m, stream);
-    if (per <= 64) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 16>(g, grid_m, stream);
+    if (per <= 16) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 4, true>(g, grid_m, stream);
+    if (per <= 32) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 8, true>(g, grid_m, stream);
+    if (per <= 64) return launch_cfg<TM, TN, WM, WN, NS, AF, EP, 1, 16, true>(g, grid_m, stream);
     return launch_cfg<TM, TN, WM, WN, NS, AF, EP>(g, grid_m, stream);
 }
 

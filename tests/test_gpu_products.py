@@ -89,10 +89,11 @@ def test_gemm_tiny_end_to_end(orc):
 # (9, 201, 2048) and (13, 75, 4096) split K four and eight ways with M N odd,
 # which takes the split-K reduce's one-output-per-thread path; (9, 256,
 # 131072) gives each workgroup 128 K steps, more than the small-M tiles'
-# scale preload holds (64), so they load the scales per step
+# scale preload holds (64), so they load the scales per step; (9, 200, 320)
+# has 5 K steps, an odd count for the small-M tiles' two-step stages
 @pytest.mark.parametrize("M,N,K", [(1, 128, 1024), (8, 256, 512), (9, 200, 256), (37, 200, 256),
                                    (64, 384, 1024), (130, 384, 512), (256, 256, 2048), (300, 136, 640),
-                                   (9, 201, 2048), (13, 75, 4096), (9, 256, 131072)])
+                                   (9, 201, 2048), (13, 75, 4096), (9, 256, 131072), (9, 200, 320)])
 def test_gemm_shapes(orc, M, N, K):
     _gemm_case(orc, M, N, K, seed=M * 7 + N)
 
