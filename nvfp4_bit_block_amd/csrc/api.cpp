@@ -45,9 +45,12 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
     // The VALU GEMV wins while its activation slice fits in registers (M <= 4,
-    // the K = 2048 and 16384 layouts up to M = 8) or in LDS (short rows);
-    // beyond that the MFMA tiles are faster.
-    if (M <= 4 || (M <= 8 && (K <= 4096 || K == 16384))) {
+    // the K = 2048 layout up to M = 8) or in LDS (short rows); beyond that the
+    // MFMA tiles are faster.  On o_proj (K = 16384) the GEMV costs about 3 us
+    // per row (19 us at M = 4, 31 us at M = 8) while the 32-row tile with its
+    // scale preload costs about 26 us at any M up to 32, so the tile takes
+    // M >= 7 there (M = 8: W4A4 35.6 -> 26.0 us, W4A16 31.5 -> 26.3 us).
+    if (M <= 4 || (M <= 8 && K <= 4096) || (M <= 6 && K == 16384)) {
         p.gemv = true;
         return p;
     }
