@@ -15,8 +15,10 @@
 //     conversion (one instruction per two elements) and multiplied with the
 //     activation by v_dot2_f32_bf16, one fp32 partial per 16-element block,
 //     scaled once per block;
-//   * the activation is read once per workgroup: kept in VGPRs when a lane's
-//     slice is small (NCH * M <= 2 chunks), else staged in LDS;
+//   * the activation is read once per workgroup: k_gemv (the K = 2048 and
+//     K = 16384 layouts) holds each lane's slice of it in VGPRs for every
+//     M <= 8; k_gemv_any (other K) stages it in LDS when M * K * 2 <= 64 KB
+//     and reads it from global memory otherwise;
 //   * row sums are reduced across the wave with cross-lane shuffles.
 // Weights are read with non-temporal loads: each byte is used once.
 #include "nvfp4_device.hpp"
