@@ -29,7 +29,8 @@
  *   - Scalars that live with the tensors (global scales, input_scale) are
  *     device pointers to fp32, so no call reads device memory on the host.
  *   - The caller allocates and frees every buffer, workspace included; the
- *     library allocates no memory and keeps no device state between calls.
+ *     library allocates no memory and keeps no device state between calls,
+ *     except the 4 KB static scratch array of nvfp4_quantize_noalloc.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without waiting for it.  Outputs must not alias
  *     inputs.  Calls on the same stream are ordered; a workspace must not be
@@ -91,6 +92,26 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 int32_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
                        uint8_t* codes, uint8_t* scales, float* global_scale, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantize without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and checks as nvfp4_quantize
+ * without the workspace; bit-identical output.
+ *
+ * Dynamic mode keeps its pass-1 partial maxima in a static device array of
+ * 1024 uint32 (4 KB) that each GPU holds from the first call until the
+ * process ends (amax_grid never needs more than 768 of them, so no shape the
+ * dynamic quantize accepts is refused for its size; a rows * cols product
+ * past 2^62 is UNSUPPORTED).  The first call on a device resolves the array's
+ * address there (hipGetSymbolAddress, with the stream's device current); the
+ * call never allocates or frees memory.  Every call on a GPU shares that
+ * GPU's array: calls that can overlap on one GPU (different streams, no
+ * ordering between them) race and must not be issued.  Static mode uses no
+ * scratch at all.
+ * ------------------------------------------------------------------------ */
+int32_t nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
+                               uint8_t* codes, uint8_t* scales, float* global_scale, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dequantize  ("Getting GLM-5.2 NVFP4 Post-Training off the ground", "Going

@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "nvfp4_last_error": (ctypes.c_char_p, []),
             "nvfp4_quantize_workspace_size": (SZ, [I64, I64]),
             "nvfp4_quantize": (I32, [P, I64, I64, P, P, P, P, P, SZ, P]),
+            "nvfp4_quantize_noalloc": (I32, [P, I64, I64, P, P, P, P, P]),
             "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, P]),
             "nvfp4_gemv_w4a16": (I32, [P, I64, I64, I64, P, P, P, P, P]),
             "nvfp4_gemm_w4a4_workspace_size": (SZ, [I64, I64, I64]),

@@ -266,6 +266,31 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const floa
     return hip_status(launch_quantize_pack(a, s), "quantize pack");
 }
 
+int32_t nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
+                               uint8_t* codes, uint8_t* scales, float* global_scale, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows < 0 || cols <= 0 || cols % 16 != 0)
+        return fail(NVFP4_ERR_SHAPE, "quantize_noalloc: need rows >= 0, cols > 0 and cols %% 16 == 0%s");
+    if (rows > ((int64_t)1 << 62) / cols)
+        return fail(NVFP4_ERR_UNSUPPORTED, "quantize_noalloc: rows * cols overflows%s");
+    if (!static_scale && amax_grid(rows * cols) > kNoAllocPartials)
+        return fail(NVFP4_ERR_UNSUPPORTED, "quantize_noalloc: more partial maxima than the static scratch holds%s");
+    if (rows == 0) return NVFP4_OK;
+    if (!x || !codes || !scales || !global_scale)
+        return fail(NVFP4_ERR_NULL_ARG, "quantize_noalloc: x, codes, scales and global_scale are required%s");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(global_scale) ||
+        (static_scale && !aligned4(static_scale)))
+        return fail(NVFP4_ERR_ALIGN, "quantize_noalloc: pointers must be 16-byte aligned%s");
+    hipStream_t s = as_stream(stream);
+    if (static_scale)   // one pass, no scratch
+        return nvfp4_quantize(x, rows, cols, static_scale, codes, scales, global_scale, nullptr, 0, stream);
+    uint32_t* partial = nullptr;
+    int32_t st = hip_status(noalloc_partials(s, &partial), "quantize_noalloc scratch");
+    if (st) return st;
+    return nvfp4_quantize(x, rows, cols, nullptr, codes, scales, global_scale, partial,
+                          (size_t)kNoAllocPartials * sizeof(uint32_t), stream);
+}
+
 int32_t nvfp4_quantize_columnwise(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
                                   uint8_t* codes_t, uint8_t* scales_t, float* global_scale, void* workspace,
                                   size_t workspace_bytes, void* stream) {

@@ -46,6 +46,12 @@ struct PackArgs {
 
 hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, int grid,
                                hipStream_t stream);
+
+// The no-alloc quantize keeps its pass-1 partial maxima in a static device
+// array of kNoAllocPartials entries per GPU (quantize.hip); *out receives its
+// device address on the device of `stream` (the current device for NULL).
+constexpr int kNoAllocPartials = 1024;
+hipError_t noalloc_partials(hipStream_t stream, uint32_t** out);
 hipError_t launch_quantize_pack(const PackArgs& a, hipStream_t stream);
 
 // y = bf16(fl(fl(q*s) * Sg)); Sg = *sg_ptr, or `sg_const` when sg_ptr is null.

@@ -17,6 +17,8 @@
 #include "nvfp4_encode.hpp"
 #include "nvfp4_internal.hpp"
 
+#include <mutex>
+
 // Bit-exactness needs every fp32 step rounded on its own: no contraction.
 #pragma clang fp contract(off)
 
@@ -224,6 +226,51 @@ int grid_for(int64_t work, int per_block, int cap) {
 // workgroups 114 us against 131 us with 1024 and 130 us with 512 (a thread's
 // successive loads are grid x 8 KB apart: 6 MB rather than a power of two).
 int amax_grid(int64_t n) { return grid_for(n / 8, kAmaxThreads * kAmaxUnroll, 768); }
+
+// ----------------------------------------------------------- no-alloc scratch --
+//
+// Device memory of nvfp4_quantize_noalloc: the pass-1 partial maxima, at most
+// kNoAllocPartials of them (amax_grid never exceeds 768).  Each GPU the
+// library runs on holds its own copy until the process ends; every call on a
+// GPU shares it, so calls that overlap on one GPU race (each call overwrites
+// every entry it reads, so nothing needs clearing between calls).  Host code
+// never passes the name `scratch` to a kernel: there it is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint32_t scratch[kNoAllocPartials];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_partials(hipStream_t stream, uint32_t** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // resolve the array's address once per device, with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, int grid,
                                hipStream_t stream) {

@@ -20,7 +20,7 @@ MIS = 4097        # misaligned
 def test_exports_every_header_symbol():
     L = ctypes.CDLL(nv.LIB_PATH)
     names = nv.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
 
@@ -47,6 +47,19 @@ def test_quantize_validation():
     assert q(None, 0, 32, None, None, None, None, None, 0, None) == OK   # empty ignores pointers
     assert L.nvfp4_quantize_workspace_size(65536, 6144) > 0
     assert b"cols" in L.nvfp4_last_error() or True
+
+
+def test_quantize_noalloc_validation():
+    q = nv.lib().nvfp4_quantize_noalloc
+    q.restype = ctypes.c_int32
+    q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5
+    assert q(None, 4, 32, None, A, A, A, None) == NULL
+    assert q(A, 4, 33, None, A, A, A, None) == SHAPE
+    assert q(A, -1, 32, None, A, A, A, None) == SHAPE
+    assert q(A, 1 << 62, 32, None, A, A, A, None) == UNSUP           # rows * cols overflows
+    assert q(MIS, 4, 32, None, A, A, A, None) == ALIGN
+    assert q(A, 4, 32, MIS, A, A, A, None) == ALIGN
+    assert q(A, 0, 32, None, None, None, None, None) == OK           # empty: no-op
 
 
 def test_dequantize_validation():
