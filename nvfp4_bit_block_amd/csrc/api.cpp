@@ -598,8 +598,15 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
     g1.row_off = row_off;
     g1.tile_off = tile_off;
     g1.groups = E;
-    g1.out = h;
+    // W4A4: the gate/up epilogue quantizes h under a2_scale itself and writes
+    // the down projection's operand (f16 q * s); the bf16 h is kept only for
+    // the LoRA down projection's shared A, which reads it
+    g1.out = (p->mode == 1 && !lora2) ? nullptr : h;
     g1.ldo = p->I;
+    if (p->mode == 1) {
+        g1.out_q = at<uint16_t>(workspace, l.hq);
+        g1.q_global = t->a2_scale;
+    }
     g1.half_n = p->I;
     AFmt af = AFmt::kBf16;
     if (p->mode == 1) {
@@ -659,19 +666,7 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
     g2.ldo = p->H;
     g2.a_src_rows = S;
     if (p->mode == 1) {
-        uint16_t* hq = at<uint16_t>(workspace, l.hq);
-        PackArgs a;
-        a.x = h;
-        a.rows = S;
-        a.cols = p->I;
-        a.rows_valid = row_off + E;
-        a.mode = ScaleMode::kGrouped;
-        a.sg_group = t->a2_scale;
-        a.row_group = pos_group;
-        a.xhat = hq;
-        st = hip_status(launch_quantize_pack(a, s), "moe intermediate quantize");
-        if (st) return st;
-        g2.a = hq;
+        g2.a = at<uint16_t>(workspace, l.hq);   // written by GEMM 1's epilogue
         g2.a_global = t->a2_scale;
     } else {
         g2.a = h;

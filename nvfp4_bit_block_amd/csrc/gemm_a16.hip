@@ -37,6 +37,7 @@
 // consecutive rows fall on distinct banks: A row r keeps its chunk c in slot
 // c ^ ((r / 2) % 8), B column n its code half h in slot h ^ ((n / 8) % 2).
 #include "nvfp4_device.hpp"
+#include "nvfp4_encode.hpp"
 #include "nvfp4_internal.hpp"
 
 namespace nvfp4 {
@@ -558,22 +559,43 @@ void k_gemm_a16(GemmArgs g) {
         if (nmain + u < nsteps) step(nmain + u, u);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32
+    // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32.
+    // Gate/up with out_q also quantizes h to NVFP4 under q_global[group]:
+    // the 16 lanes of a DPP row (lane / 16 fixed) hold the 16 consecutive
+    // columns of one block of one row, so the block maximum is a 16-lane
+    // reduction, and each lane encodes its own element with the quantizer's
+    // rule (nvfp4_encode.hpp) and stores the exact product q * s as f16.
+    float sgq = 0.0f;
+    if constexpr (kGateUp) {
+        if (g.out_q) sgq = g.q_global[gi];
+    }
+    const float tq = 6.0f * sgq;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t row = row_beg + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+            // (the row depends on the lane only through hf, so the 16-lane
+            // groups of the gate/up quantization below stay whole)
             if (row >= row_end) continue;
             if constexpr (kGateUp) {
 #pragma unroll
                 for (int j = 0; j < TN / 2; ++j) {
+                    // half_n is a multiple of 64, so a 16-column block is wholly in or out
                     const int64_t hcol = (int64_t)tn * (BN / 2) + wn * (WTN / 2) + 32 * j + c32;
-                    if (hcol >= g.half_n) continue;
+                    const bool ok = hcol < g.half_n;
                     const float gv = acc[i][j][r] * sc;
                     const float uv = acc[i][j + TN / 2][r] * sc;
                     const float hv = gv / (1.0f + expf(-gv)) * uv;
-                    reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + hcol] = (uint16_t)f32_to_bf16_rne(hv);
+                    const uint32_t hb = f32_to_bf16_rne(hv);
+                    if (g.out != nullptr && ok) reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + hcol] = (uint16_t)hb;
+                    if (g.out_q != nullptr) {
+                        const BlockEnc be = block_enc(row16_max_u32(hb & 0x7FFFu), sgq, tq);
+                        const uint32_t code = encode_one(hb, be);
+                        const f16x2 qv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0);
+                        const _Float16 v = qv.x * (_Float16)be.s;
+                        if (ok) g.out_q[row * g.ldo + hcol] = __builtin_bit_cast(uint16_t, v);
+                    }
                 }
             } else {
 #pragma unroll

@@ -129,6 +129,21 @@ __device__ __forceinline__ float dpp_f32(float v) {
                                                                  ROW_MASK, 0xF, true));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Maximum over each row of 16 lanes (lanes 16 q .. 16 q + 15), returned in
+// every lane of the row; all lanes of the row must be active.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]: quad maxima
+    v = max(v, dpp_u32<0x141>(v));   // row_half_mirror: 8-lane maxima
+    v = max(v, dpp_u32<0x140>(v));   // row_mirror: 16-lane maxima
+    return v;
+}
+
 // Sum over the 64 lanes of a wave with six DPP adds; the total lands in
 // lane 63 (other lanes hold partial sums).
 __device__ __forceinline__ float wave_sum_lane63(float v) {

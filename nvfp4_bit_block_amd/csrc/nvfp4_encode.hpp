@@ -52,6 +52,40 @@ __device__ __forceinline__ uint32_t encode_pair(uint32_t acc, uint32_t w, float 
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, ql, qh, 1.0f, SEL);
 }
 
+// The per-block half of the encoder, for kernels that hold one element of a
+// block per lane: the scale byte, its value s, the divisor d = s * Sg and
+// whether the reciprocal quotient applies (the block-level condition of
+// encode_block below), given the block's magnitude maximum as a bf16 pattern.
+struct BlockEnc {
+    uint32_t s8;
+    float s, d, y;
+    bool fast;
+};
+
+__device__ __forceinline__ BlockEnc block_enc(uint32_t max_bits, float Sg, float t) {
+#pragma clang fp contract(off)
+    const float bmax = bf16_to_f32(max_bits);
+    const float s_f = (t > 0.0f) ? bmax / t : 0.0f;
+    BlockEnc b;
+    b.s8 = e4m3_from_f32(s_f);
+    b.s = e4m3_to_f32(b.s8);
+    b.d = b.s * Sg;
+    b.fast = b.d >= 0x1p-100f && b.d < 0x1p125f && bmax <= 8.0f * b.d;
+    b.y = b.fast ? 1.0f / b.d : 0.0f;
+    return b;
+}
+
+// The 4-bit code (sign in bit 3) of one bf16 element h of a block, with the
+// same quotient and rounding as encode_block.
+__device__ __forceinline__ uint32_t encode_one(uint32_t h, const BlockEnc& b) {
+#pragma clang fp contract(off)
+    if (b.fast) {
+        const float q = div_e2m1(bf16_to_f32(h & 0xFFFFu), b.d, b.y);
+        return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, 0.0f, 1.0f, 0) & 0xFu;
+    }
+    return encode_elem(h & 0xFFFFu, b.d);
+}
+
 // One 16-element block: 8 words of bf16 pairs -> 8 code bytes + scale byte.
 __device__ __forceinline__ uint32_t encode_block(const uint32_t w[8], float Sg, float t, uint2& out) {
 #pragma clang fp contract(off)

@@ -110,7 +110,7 @@ enum class AFmt : int { kBf16 = 0, kF16 = 2 };
 enum class Epi : int {
     kStoreBf16 = 0,   // y = bf16(acc * scale)
     kPartialF32 = 1,  // partial[split] = acc (split-K, reduced later)
-    kMoeGateUp = 2,   // h = bf16(silu(g*scale) * (u*scale))
+    kMoeGateUp = 2,   // h = bf16(silu(g*scale) * (u*scale)) (and its NVFP4 q * s with out_q)
     kMoeDown = 3,     // Y = acc * scale (fp32)
     kMoeGateUpLora = 4,  // kMoeGateUp with the LoRA overlay added before the activation
     kMoeDownLora = 5,    // kMoeDown with the LoRA overlay
@@ -137,6 +137,12 @@ struct GemmArgs {
     // output
     void* out = nullptr;
     int64_t ldo = 0;
+    // gate/up epilogues only: when out_q is set, h is also NVFP4-quantized
+    // under the per-group static scale q_global[group] (blocks of 16 along
+    // the row) and written to out_q [*, ldo] as the exact f16 products q * s,
+    // the operand of the down projection; out (bf16 h) may then be null.
+    uint16_t* out_q = nullptr;
+    const float* q_global = nullptr;
     int32_t ksplit = 1;
     int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
     // LoRA overlay (the kMoe*Lora epilogues, ksplit 1): the
