@@ -466,6 +466,7 @@ def main():
                                 flops=2.0 * M * N * K, info={"M": M, "N": N, "K": K}))
 
     # ----------------------------------------------------------------- MoE --
+    moe_host = None
     if "moe" in groups:
         T, E, k, H, I = wl.MOE_T, wl.MOE_E, wl.MOE_TOPK, wl.MOE_H, wl.MOE_I
         ids, wts = wl.moe_routing(T, E, k, seed=5)
@@ -495,6 +496,18 @@ def main():
         a13[:] = tmp[0]
         s2 = H * 0.02 ** 2
         a2 = torch.full((E,), 2.0 * s2 * float(np.log(T * k * I)) / 2688.0, dtype=torch.float32, device=dev)
+        def moe_host(ts=4):
+            # the first ts tokens and the experts they use (renumbered), for
+            # the CPU baseline
+            used = sorted(set(int(e) for e in ids[:ts].ravel()))
+            remap = {e: i for i, e in enumerate(used)}
+            idx = torch.tensor(used, device=dev)
+            pick = lambda t: t.index_select(0, idx).cpu().numpy()
+            return {"x": xm[:ts].view(torch.int16).cpu().numpy().view(np.uint16),
+                    "ids": np.vectorize(remap.get)(ids[:ts]).astype(np.int32), "wts": wts[:ts],
+                    "w": [pick(t) for t in (w13c, w13s, w13g, w2c, w2s, w2g)], "a13": pick(a13), "a2": pick(a2),
+                    "tokens": T, "experts": len(used)}
+
         moe_bytes = E * (2 * I * H + H * I) * (0.5 + 1 / 16) + 2 * T * H * 2
         moe_flops = 2.0 * T * k * (2 * I * H + H * I)
         for mode in (0, 1):
@@ -620,7 +633,17 @@ def main():
                     "bytes_per_launch": 6144 * 16384 // 2 + 6144 * 16384 // 16,
                     "us_per_launch": head["us_per_launch"]}
     progress("timed steps done")
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu = None
+    if not args.no_cpu_baseline:
+        host = {}
+        if layers:
+            host["layers"] = {name: (cs[0][0].cpu().numpy(), cs[0][1].cpu().numpy(), np.float32(cs[0][2].item()),
+                                     x8.view(torch.int16).cpu().numpy().view(np.uint16))
+                              for name, (N, K, cs, x8) in layers.items()}
+        if moe_host is not None:
+            host["moe"] = moe_host()
+        cpu = cpu_baseline(args.cpu_seconds, host)
+        progress("cpu baseline done")
     line = {
         "metric": METRIC, "value": None if value is None else round(value, 4), "unit": "TB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -663,27 +686,100 @@ class _Sleeper:
             self.torch.cuda._sleep(self.cycles)
 
 
-def cpu_baseline(target_s: float):
-    """The oracle (as it stands) on the host cores: W4A16 GEMV over the full
-    o_proj weight at batch 1, repeated until about `target_s` seconds."""
+def _cpu_model():
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(target_s: float, host=None):
+    """The oracle (as it stands) on the host cores, on bounded samples of the
+    step's workloads.  The headline value is the W4A16 GEMV over the full
+    o_proj weight at batch 1, repeated for about `target_s` seconds; the rows
+    time the other workloads once each: the GEMV at batch 1-8 on both layers
+    (full size), the quantize on the first 4096 rows of the 65536 x 6144
+    tensor, the W4A4 GEMM sweep on sampled weight rows (all M, both layers)
+    and the MoE layer in both modes on 4 sampled tokens with the experts they
+    use.  `host` carries the weights the GPU part set up (NVFP4 bytes copied
+    back), when those row groups ran."""
     import oracle
     import workloads as wl
     threads = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    w, x = wl.gemv_inputs("o_proj")
-    c, s, g = oracle.quantize(w)
-    x1 = x[:1]
+    host = host or {}
+    rows = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    layers = host.get("layers")
+    if layers is None:
+        layers = {}
+        for name in ("o_proj", "q_b_proj"):
+            w, x = wl.gemv_inputs(name)
+            layers[name] = (*oracle.quantize(w), x)
+    c, s, g, x8 = layers["o_proj"]
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemv_w4a16(x1, c, s, g)
+        oracle.gemv_w4a16(x8[:1], c, s, g)
         n += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = (time.perf_counter() - t0) / n
-    wbytes = c.nbytes + s.nbytes
-    return {"value": round(wbytes / dt / 1e12, 6), "unit": "TB/s", "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
-            "kind": "oracle", "sample": f"W4A16 GEMV o_proj 6144x16384 at M=1 (fp64 oracle incl. its dequantize), "
-                                        f"{n} calls, {dt:.3f} s per call"}
+    head = (c.nbytes + s.nbytes) / dt / 1e12
+    for name, (c, s, g, x8) in layers.items():
+        N, K = c.shape[0], c.shape[1] * 2
+        wbytes = c.nbytes + s.nbytes
+        for M in wl.GEMV_M:
+            t = timed(lambda: oracle.gemv_w4a16(x8[:M], c, s, g))
+            rows[f"gemv_w4a16_{name}_M{M}"] = {"s": round(t, 4), "TB_s": round(wbytes / t / 1e12, 6),
+                                               "sample": f"full {N}x{K}, M={M}"}
+    xq = wl.heavy_tailed(4096, 6144, seed=1)
+    t = timed(lambda: oracle.quantize(xq))
+    rows["quantize_65536x6144"] = {"s": round(t, 4), "GB_s": round(xq.size * 4.5625 / t / 1e9, 3),
+                                   "sample": "first 4096 of 65536 rows (the same draw), dynamic scale; "
+                                             "GB/s over the two-pass bytes of the sample"}
+    for name, (c, s, g, _) in layers.items():
+        N, K = c.shape[0], c.shape[1] * 2
+        for M in wl.GEMM_M_SWEEP:
+            ns = max(16, min(N, ((1 << 30) // (M * K)) // 16 * 16))
+            x = wl.activations(M, K, seed=4)
+            isc = oracle.global_scale(x)
+            t = timed(lambda: oracle.gemm_w4a4(x, isc, c[:ns], s[:ns], g))
+            rows[f"gemm_w4a4_{name}_M{M}"] = {"s": round(t, 4), "TFLOPS": round(2.0 * M * ns * K / t / 1e12, 6),
+                                              "sample": f"{ns} of {N} weight rows, M={M}, K={K}"}
+    moe = host.get("moe")
+    if moe is not None:
+        x, ids, wts, w = moe["x"], moe["ids"], moe["wts"], moe["w"]
+        ts, H, I = x.shape[0], x.shape[1], w[3].shape[2] * 2
+        flops = 2.0 * ts * ids.shape[1] * (2 * I * H + H * I)
+        for mode in (0, 1):
+            kw = {} if mode == 0 else {"a13": moe["a13"], "a2": moe["a2"]}
+            t = timed(lambda: oracle.moe(x, ids, wts, *w, mode=mode, **kw))
+            rows[f"moe_{'w4a16' if mode == 0 else 'w4a4'}"] = {
+                "s": round(t, 4), "TFLOPS": round(flops / t / 1e12, 6),
+                "sample": f"{ts} of {moe['tokens']} tokens ({ts * ids.shape[1]} slots over the {moe['experts']} "
+                          f"experts they use; the oracle dequantizes each used expert once)"}
+    return {"value": round(head, 6), "unit": "TB/s", "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"headline: W4A16 GEMV o_proj 6144x16384 at M=1 (fp64 oracle incl. its dequantize), "
+                      f"{n} calls, {dt:.3f} s per call; rows: the other workloads, one call each on the stated "
+                      f"samples", "rows": rows}
 
 
 if __name__ == "__main__":

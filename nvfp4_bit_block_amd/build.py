@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "quantize.hip", "transpose.hip", "gemv.hip", "gemm_a16.hip", "moe.hip", "lora.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "transpose.hip", "gemv.hip", "gemm_a16.hip", "gemm_stream.hip", "moe.hip", "lora.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -85,6 +85,77 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+// The weight-streaming MFMA kernel (gemm_stream.hip) for small batches.
+// Measured on MI355X with NVFP4 weights rotated through HBM: where a weight
+// row holds at most four 1024-K chunks (q_b_proj, 16384 x 2048) it beats
+// both the GEMV (from M = 3) and the LDS-staged tiles up to M = 64 (W4A4 on
+// a packed activation: M = 8 16.3 -> 7.9 us, M = 32 22.9 -> 10.0 us,
+// M = 64 23.1 -> 13.7 us; W4A16 M = 8 15.1 -> 8.5 us, M = 64 22.1 ->
+// 17.8 us); on long rows (o_proj, 6144 x 16384) it wins for the packed
+// activation at M = 5..16 (M = 8 25.3 -> 21.2 us, M = 16 26.2 -> 22.6 us)
+// and not for bf16 activations, whose registers limit a workgroup to half
+// the row.
+struct StreamPlan {
+    bool use = false;
+    int nb = 4, mb = 1, ksplit = 1;
+    int64_t krange = 0;
+};
+
+StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
+    StreamPlan p;
+    if (M < 1 || M > 64 || N < 1 || K % 128 != 0 || N * (K / 2) >= kMaxOperandBytes || M * K * 2 >= kMaxOperandBytes)
+        return p;
+    const bool short_k = K <= 4096;
+    if (short_k ? M < 3 : (am == SAct::kBf16 || M < 5 || M > 16)) return p;
+    p.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    const int maxch = stream_max_chunks(am, p.mb);
+    // the fewest K splits (partial sums cost an extra pass) that fit the
+    // activation registers and give at least 192 workgroups, wider weight
+    // tiles first (measured: 192-768 resident workgroups stream alike)
+    for (int s = 1; s <= 8; s *= 2) {
+        if (K / 128 < s) break;
+        const int64_t krange = ((K / 128 + s - 1) / s) * 128;
+        const int64_t chunks = (krange + 1023) / 1024;
+        int nch = 1;
+        while (nch < chunks) nch *= 2;
+        if (nch > maxch) continue;
+        for (int nb = 4; nb >= 2; nb -= 2) {
+            if (((N + 16 * nb - 1) / (16 * nb)) * s < 192) continue;
+            p.use = true;
+            p.nb = nb;
+            p.ksplit = s;
+            p.krange = krange;
+            return p;
+        }
+    }
+    return p;
+}
+
+hipError_t run_stream(const StreamPlan& p, SAct am, const void* a, const uint8_t* a_scales, const float* a_global,
+                      int64_t M, int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                      const float* w_global, uint16_t* y, float* partial, hipStream_t s) {
+    StreamArgs g;
+    g.a = a;
+    g.a_scales = a_scales;
+    g.a_global = a_global;
+    g.b_codes = w_codes;
+    g.b_scales = w_scales;
+    g.b_global = w_global;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.ksplit = p.ksplit;
+    g.krange = p.krange;
+    g.out = p.ksplit > 1 ? static_cast<void*>(partial) : static_cast<void*>(y);
+    hipError_t e = launch_gemm_stream(g, am, p.nb, p.mb, s);
+    if (e != hipSuccess || p.ksplit == 1) return e;
+    return launch_splitk_reduce(partial, p.ksplit, M, N, w_global, a_global, y, s);
+}
+
+size_t stream_partial_bytes(const StreamPlan& p, int64_t M, int64_t N) {
+    return p.use && p.ksplit > 1 ? align_up((size_t)p.ksplit * (size_t)(M * N) * 4) : 0;
+}
+
 // Rows of the activation handled per GEMM launch: the kernel addresses the
 // decoded activation through one buffer resource, which spans < 2 GiB.
 int64_t gemm_chunk_rows(int64_t M, int64_t K) {
@@ -97,14 +168,24 @@ struct GemmLayout {
     size_t xhat = 0, partial = 0, total = 0;
 };
 
+// W4A4 workspace: the quantized activation (exact f16 q * s for the tiles,
+// bf16 for the GEMV, packed codes and scales for the stream kernel) and the
+// split-K partial sums of whichever kernel the plans pick.
 GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
     GemmLayout l;
     const GemmPlan p = plan_gemm(M, N, K);
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
     size_t off = 0;
     l.xhat = off; off += align_up((size_t)(M * K * 2));
-    if (!p.gemv && p.ksplit > 1) {
-        const int64_t rows = gemm_chunk_rows(M, K);
-        l.partial = off; off += align_up((size_t)p.ksplit * (size_t)(rows * N) * 4);
+    size_t part = 0;
+    if (sp.use) {
+        part = stream_partial_bytes(sp, M, N);
+    } else if (!p.gemv && p.ksplit > 1) {
+        part = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
+    }
+    if (part) {
+        l.partial = off;
+        off += part;
     }
     l.total = off;
     return l;
@@ -115,7 +196,9 @@ GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
 GemmLayout layout_gemm_w4a16(int64_t M, int64_t N, int64_t K) {
     GemmLayout l;
     const GemmPlan p = plan_gemm(M, N, K);
-    if (!p.gemv && p.ksplit > 1) l.total = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
+    if (sp.use) l.total = stream_partial_bytes(sp, M, N);
+    else if (!p.gemv && p.ksplit > 1) l.total = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
     l.partial = 0;
     return l;
 }
@@ -364,6 +447,13 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
         return fail(NVFP4_ERR_NULL_ARG, "gemv: all pointers are required%s");
     if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned4(w_global) || !aligned16(y))
         return fail(NVFP4_ERR_ALIGN, "gemv: pointers must be 16-byte aligned%s");
+    // short rows from M = 3: the stream kernel (when it needs no K split, so
+    // no workspace)
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
+    if (sp.use && sp.ksplit == 1)
+        return hip_status(run_stream(sp, SAct::kBf16, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
+                                     nullptr, as_stream(stream)),
+                          "gemv stream");
     return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y,
                                         as_stream(stream)),
                       "gemv");
@@ -395,6 +485,26 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (!workspace || workspace_bytes < l.total)
         return fail(NVFP4_ERR_WORKSPACE, "gemm: workspace smaller than nvfp4_gemm_w4a4_workspace_size%s");
     hipStream_t s = as_stream(stream);
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
+    if (sp.use) {
+        // the static quantize writes the packed activation (codes, then scale
+        // bytes) into the workspace; the stream kernel decodes it in registers
+        uint8_t* ac = at<uint8_t>(workspace, l.xhat);
+        uint8_t* as = ac + align_up((size_t)(M * K / 2));
+        PackArgs a;
+        a.x = x;
+        a.rows = M;
+        a.cols = K;
+        a.mode = ScaleMode::kStatic;
+        a.sg_ptr = input_scale;
+        a.codes = ac;
+        a.scales = as;
+        int32_t st = hip_status(launch_quantize_pack(a, s), "gemm activation quantize");
+        if (st) return st;
+        return hip_status(run_stream(sp, SAct::kPacked, ac, as, input_scale, M, N, K, w_codes, w_scales, w_global, y,
+                                     sp.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                          "gemm stream");
+    }
     const GemmPlan p = plan_gemm(M, N, K);
     if (p.gemv && gemv_quantizes_activation((int)M, K))
         return hip_status(launch_gemv_w4a4(x, (int)M, N, K, w_codes, w_scales, w_global, input_scale, y, s),
@@ -446,6 +556,11 @@ int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, 
     if (!workspace || workspace_bytes < l.total)
         return fail(NVFP4_ERR_WORKSPACE, "gemm_packed: workspace smaller than nvfp4_gemm_w4a4_packed_workspace_size%s");
     hipStream_t s = as_stream(stream);
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
+    if (sp.use)
+        return hip_status(run_stream(sp, SAct::kPacked, a_codes, a_scales, a_global, M, N, K, w_codes, w_scales,
+                                     w_global, y, sp.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                          "gemm_packed stream");
     const GemmPlan p = plan_gemm(M, N, K);
     // Small M on the fixed GEMV layouts: the GEMV decodes the packed
     // activation itself (one launch).
@@ -491,6 +606,11 @@ int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
     if (l.total > 0 && (!workspace || workspace_bytes < l.total))
         return fail(NVFP4_ERR_WORKSPACE, "gemm_w4a16: workspace smaller than nvfp4_gemm_w4a16_workspace_size%s");
     hipStream_t s = as_stream(stream);
+    const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
+    if (sp.use)
+        return hip_status(run_stream(sp, SAct::kBf16, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
+                                     sp.ksplit > 1 ? static_cast<float*>(workspace) : nullptr, s),
+                          "gemm_w4a16 stream");
     const GemmPlan p = plan_gemm(M, N, K);
     if (p.gemv)
         return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y, s),

@@ -1,0 +1,393 @@
+// gemm_stream.hip -- small-batch NVFP4 GEMM that streams the weights:
+// Y [M, N] = A [M, K] * W^T with W NVFP4 [N, K] and M <= 64.
+//
+// The weight-streaming regime of the W4A4 batch sweep and of W4A16 at
+// small batch (model card "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "Kernel
+// choice"; Fprop with the contraction axis innermost, "Getting GLM-5.2 NVFP4
+// Post-Training off the ground", "TN, NT, and what actually binds").  At
+// these M the product is bound by the weight bytes, so the kernel is built
+// like a GEMV that multiplies on the matrix cores:
+//
+//   * a workgroup (8 waves) owns BN = 16 NB weight rows and a range of K
+//     (the whole K, or 1/S of it under a K split); the launcher sizes the
+//     grid so that every workgroup is resident at once, and the weight
+//     stream never waits for a second round of workgroups;
+//   * the weights move from HBM straight into LDS (buffer_load ... lds, each
+//     instruction 1 KB of two contiguous 512-byte row pieces, or 256 bytes of
+//     scales), in chunks of 1024 K through an NS-stage ring, NS - 1 chunks
+//     in flight;
+//   * the activation slice a wave needs for the whole K range is loaded into
+//     registers once, before the weights (so the ring's vmcnt waits never
+//     wait on it): as 16-bit values (bf16 for W4A16, or the f16 products
+//     q * s of an already quantized activation), as packed NVFP4 codes and
+//     scale bytes decoded to exact f16 q * s at use, or as bf16 values that
+//     the wave quantizes in registers under the static input scale with the
+//     quantizer's block rule (then kept as packed codes);
+//   * K is split across the 8 waves (wave w takes K [128 w, 128 w + 128) of
+//     every chunk, so each activation element is loaded once per
+//     workgroup); a wave decodes its weight fragments from LDS to exact q * s
+//     and runs v_mfma_f32_16x16x32_{f16,bf16} with the weights as the A
+//     operand (16 weight rows) and the activation as B (16 batch rows);
+//   * the eight wave partials meet in LDS and are summed in wave order; the
+//     workgroup writes bf16 Y (scaled by both global scales) or, under a K
+//     split, an fp32 partial that the split-K reduction sums in split order.
+//
+// K order: lane l of a 16x16x32 MFMA supplies row l % 16 of its operand at
+// K group l / 16 (8 values).  The same K permutation is applied to both
+// operands: in a wave's 128-K unit, lane group g takes the 32 consecutive K
+// [32 g, 32 g + 32) (two NVFP4 blocks, 16 code bytes) and MFMA kk of the
+// unit uses [32 g + 8 kk, +8).  A lane thus reads one 16-byte code chunk and
+// two scale bytes per weight row block, and holds whole blocks of its own
+// activation row.
+//
+// LDS layout of a stage: codes [BN rows][32 slots of 16 B], row r keeping
+// its chunk u in slot u ^ (r % 8); scales [BN rows][16 dwords], row r
+// keeping dword d in slot d ^ (r % 16).  Both keep the fragment reads of 16
+// consecutive rows on distinct banks.
+#include "nvfp4_device.hpp"
+#include "nvfp4_dma.hpp"
+#include "nvfp4_encode.hpp"
+#include "nvfp4_internal.hpp"
+
+#include <type_traits>
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kChunkK = 1024;          // K per ring stage: 128 per wave
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t word4(const uint4& v, int k) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Eight weight codes -> eight MFMA operand values q * s (exact).
+__device__ __forceinline__ f16x8 decode8(uint32_t w, float s, f16x8*) { return fp4x8_scaled_f16(w, (_Float16)s); }
+__device__ __forceinline__ bf16x8 decode8(uint32_t w, float s, bf16x8*) {
+    return __builtin_bit_cast(bf16x8, fp4x8_scaled_bf16_bits(w, s));
+}
+
+// Wait until at most n vector memory operations of this wave are in flight
+// (n a multiple of the per-stage load count, at most NS - 2 stages).
+template <int L>
+__device__ __forceinline__ void wait_stages(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(L)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L)); break;
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * L)); break;
+    }
+}
+
+// NB: 16-row weight blocks per workgroup (2 or 4); MB: 16-row batch blocks
+// (M <= 16 MB); NS: ring stages (2..5); NCH: the most 1024-K chunks a
+// workgroup's K range may hold (sizes the activation registers).
+template <int NB, int MB, SAct AM, int NS, int NCH>
+__global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
+    using Op = typename std::conditional<AM == SAct::kBf16, bf16x8, f16x8>::type;
+    constexpr bool kPk = AM == SAct::kPacked || AM == SAct::kQuant;   // activation kept packed
+    constexpr int BN = 16 * NB;
+    constexpr int CODE_BYTES = BN * 512, STAGE = BN * (512 + 64);
+    constexpr int LC = BN / 16, LS = BN / 32, L = LC + LS;   // DMA loads per wave per stage
+    constexpr int ROWS = 16 * MB, RSTR = BN + 4;             // reduction buffer [wave][row][RSTR] fp32
+    constexpr int RED_BYTES = kWaves * ROWS * RSTR * 4;
+    constexpr int LDS = NS * STAGE > RED_BYTES ? NS * STAGE : RED_BYTES;
+    static_assert(NB == 2 || NB == 4, "whole DMA loads per wave");
+    static_assert(NS >= 2 && NS <= 5 && LDS <= 160 * 1024, "LDS");
+    static_assert(L * (NS - 2) <= 63, "vmcnt");
+    __shared__ __align__(1024) uint8_t smem[LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i16 = lane & 15, grp = lane >> 4;
+
+    const int64_t N = g.N, K = g.K, M = g.M;
+    const int ntn = (int)((N + BN - 1) / BN);
+    const int tn = (int)blockIdx.x % ntn, kz = (int)blockIdx.x / ntn;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t k0 = (int64_t)kz * g.krange;
+    const int64_t k1 = min(K, k0 + g.krange);
+    const int nchunks = (int)((k1 - k0 + kChunkK - 1) / kChunkK);   // 1 .. NCH (launcher)
+    const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);
+    const u32x4 rb_c = make_rsrc(g.b_codes, (uint64_t)N * KB);
+    const u32x4 rb_s = make_rsrc(g.b_scales, (uint64_t)N * KS);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+
+    // ---- 1. the first NS - 1 chunks of weights into the ring
+    // chunk c into stage st: code load q = w LC + u covers rows 2q, 2q + 1
+    // (lane / 32), slot lane % 32 <- chunk (lane % 32) ^ (row % 8); scale load
+    // q = w LS + u covers rows 4q .. 4q + 3 (lane / 16), dword slot lane % 16
+    // <- dword (lane % 16) ^ (row % 16).  Pieces past N or past the K range
+    // read zeros.
+    auto issue = [&](int c, int st) {
+        const uint32_t base = lds0 + (uint32_t)(st * STAGE);
+        const int64_t kc = k0 + (int64_t)c * kChunkK;
+#pragma unroll
+        for (int u = 0; u < LC; ++u) {
+            const int q = w * LC + u, r = 2 * q + (lane >> 5);
+            const int unit = (lane & 31) ^ (r & 7);
+            const int64_t n = n0 + r, kk = kc + 32 * unit;
+            const uint32_t v = (n < N && kk < k1) ? (uint32_t)n * KB + (uint32_t)(kk / 2) : kOob;
+            lds_load16(rb_c, v, 0u, base + (uint32_t)(q * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < LS; ++u) {
+            const int q = w * LS + u, r = 4 * q + (lane >> 4);
+            const int d = (lane & 15) ^ (r & 15);
+            const int64_t n = n0 + r, kk = kc + 64 * d;
+            const uint32_t v = (n < N && kk < k1) ? (uint32_t)n * KS + (uint32_t)(kk / 16) : kOob;
+            lds_load4(rb_s, v, 0u, base + (uint32_t)(CODE_BYTES + q * 256));
+        }
+    };
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s)
+        if (s < nchunks) issue(s, s);
+
+    // ---- 2. activation loads: this wave's 128-K unit of every chunk, rows
+    // 16 mb + i16, as unconditional buffer loads (zeros past M or past the K
+    // range), then one wait for everything issued so far.  (The compiler
+    // tracks these loads but not the asm weight loads, so the first use of
+    // the activation has to follow a full wait; from here on the K loop
+    // issues weight loads only and waits for them itself.)
+    constexpr int XN = kPk ? 1 : NCH, XM = kPk ? 1 : MB;
+    constexpr int QN = AM == SAct::kQuant ? NCH : 1, QM = AM == SAct::kQuant ? MB : 1;
+    constexpr int PN = kPk ? NCH : 1, PM = kPk ? MB : 1;
+    uint4 xa[XN][XM][4];      // 16-bit activation values (kBf16, kF16)
+    uint4 xq[QN][QM][4];      // bf16 staging of the in-register quantization (kQuant)
+    uint4 xc[PN][PM];         // packed codes (kPacked, kQuant)
+    uint32_t xs[PN][PM];      // their two scale bytes
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.a), (short)0, (int)(AM == SAct::kPacked ? M * K / 2 : M * K * 2), (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.a_scales), (short)0, (int)(AM == SAct::kPacked ? M * K / 16 : 0), (int)kRsrcWord3);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t ku = k0 + (int64_t)c * kChunkK + 128 * w;     // the wave's unit (uniform)
+        const bool kin = c < nchunks && ku < k1;
+        const int64_t ka = ku + 32 * grp;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int64_t m = 16 * mb + i16;
+            const bool in = kin && m < M;
+            if constexpr (AM == SAct::kPacked) {
+                const uint32_t oc = in ? (uint32_t)(m * (K / 2) + ka / 2) : kOob;
+                const uint32_t os = in ? (uint32_t)(m * (K / 16) + ka / 16) : kOob;
+                xc[c][mb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, oc, 0, 0));
+                xs[c][mb] = __builtin_amdgcn_raw_buffer_load_b16(ras, os, 0, 0);
+            } else {
+                const uint32_t o = in ? (uint32_t)((m * K + ka) * 2) : kOob;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint4 v = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, in ? o + 16u * p : kOob, 0, 0));
+                    if constexpr (AM == SAct::kQuant) xq[c][mb][p] = v;
+                    else xa[c][mb][p] = v;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+    // ---- 3. in-register quantization (kQuant): each lane encodes its two
+    // 16-element blocks per unit under the static scale
+    if constexpr (AM == SAct::kQuant) {
+        const float sg = *g.a_global, t = 6.0f * sg;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                uint32_t s2 = 0;
+                uint2 c0 = make_uint2(0, 0), c1 = make_uint2(0, 0);
+                const uint4* v = xq[c][mb];
+                const uint32_t b0[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+                const uint32_t b1[8] = {v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+                s2 = encode_block(b0, sg, t, c0);
+                s2 |= encode_block(b1, sg, t, c1) << 8;
+                xc[c][mb] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+                xs[c][mb] = s2;
+            }
+    }
+    __syncthreads();
+
+    // ---- 4. the K loop
+    f32x4 acc[NB][MB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t fcode = (uint32_t)(i16 * 512 + 16 * ((4 * w + grp) ^ (i16 & 7)));
+    const uint32_t fscale = (uint32_t)(CODE_BYTES + i16 * 64 + 4 * ((2 * w + (grp >> 1)) ^ i16) + 2 * (grp & 1));
+
+    auto compute = [&](int c, int st) {
+        const uint8_t* sb = smem + st * STAGE;
+        uint4 cw[NB];
+        f32x2 sw[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            cw[nb] = *reinterpret_cast<const uint4*>(sb + fcode + nb * 16 * 512);
+            sw[nb] = e4m3x2_to_f32(*reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * 64));
+        }
+        f32x2 xsc[MB];
+        if constexpr (kPk) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            Op bx[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
+                else bx[mb] = __builtin_bit_cast(Op, xa[c][mb][kk]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const Op av = decode8(word4(cw[nb], kk), kk < 2 ? sw[nb].x : sw[nb].y, (Op*)nullptr);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16(av, bx[mb], acc[nb][mb]);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (c < nchunks) {
+            // refill the stage multiplied in iteration c - 1 (all waves passed
+            // the barrier after it)
+            if (c + NS - 1 < nchunks) issue(c + NS - 1, (c + NS - 1) % NS);
+            if (k0 + (int64_t)c * kChunkK + 128 * w < k1) compute(c, c % NS);
+            if (c + 1 < nchunks) {
+                wait_stages<L>(min(NS - 2, nchunks - 2 - c));
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- 5. wave partials -> LDS (the ring is free once every wave is here)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            *reinterpret_cast<f32x4*>(red + (w * ROWS + 16 * mb + i16) * RSTR + 16 * nb + 4 * grp) = acc[nb][mb];
+    __syncthreads();
+
+    // ---- 6. sum in wave order; thread e takes batch row e / (BN/4) and four
+    // consecutive weight rows
+    constexpr int NG = BN / 4;
+    const float scale = (g.a_global ? *g.a_global : 1.0f) * *g.b_global;
+    for (int e = tid; e < ROWS * NG; e += kThreads) {
+        const int mr = e / NG, ng = e - mr * NG;
+        f32x4 s = *reinterpret_cast<const f32x4*>(red + mr * RSTR + 4 * ng);
+#pragma unroll
+        for (int v = 1; v < kWaves; ++v) s += *reinterpret_cast<const f32x4*>(red + (v * ROWS + mr) * RSTR + 4 * ng);
+        const int64_t m = mr, n = n0 + 4 * ng;
+        if (m >= M || n >= N) continue;
+        if (g.ksplit > 1) {
+            float* o = reinterpret_cast<float*>(g.out) + ((int64_t)kz * M + m) * N + n;
+            if (n + 4 <= N && (N & 3) == 0) {
+                *reinterpret_cast<f32x4*>(o) = s;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) o[r] = s[r];
+            }
+        } else {
+            uint16_t* o = reinterpret_cast<uint16_t*>(g.out) + m * N + n;
+            const uint32_t b0 = f32_to_bf16_rne(s[0] * scale), b1 = f32_to_bf16_rne(s[1] * scale);
+            const uint32_t b2 = f32_to_bf16_rne(s[2] * scale), b3 = f32_to_bf16_rne(s[3] * scale);
+            if (n + 4 <= N && (N & 3) == 0) {
+                *reinterpret_cast<uint2*>(o) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            } else {
+                const uint32_t b[4] = {b0, b1, b2, b3};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) o[r] = (uint16_t)b[r];
+            }
+        }
+    }
+}
+
+constexpr int kActBudget = 128;   // activation VGPRs per wave
+constexpr int act_regs(SAct am, int mb) { return (am == SAct::kPacked ? 5 : 16) * mb; }
+
+template <int NB, int MB, SAct AM, int NCH>
+hipError_t launch_one(const StreamArgs& g, hipStream_t stream) {
+    if constexpr (NCH * act_regs(AM, MB) > kActBudget) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr int NS = NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
+        const int64_t ntn = (g.N + 16 * NB - 1) / (16 * NB);
+        hipLaunchKernelGGL((k_gemm_stream<NB, MB, AM, NS, NCH>), dim3((unsigned)(ntn * g.ksplit)), dim3(kThreads),
+                           0, stream, g);
+        return hipGetLastError();
+    }
+}
+
+template <int NB, int MB, SAct AM>
+hipError_t launch_nch(const StreamArgs& g, int nch, hipStream_t stream) {
+    switch (nch) {
+        case 1: return launch_one<NB, MB, AM, 1>(g, stream);
+        case 2: return launch_one<NB, MB, AM, 2>(g, stream);
+        case 4: return launch_one<NB, MB, AM, 4>(g, stream);
+        case 8: return launch_one<NB, MB, AM, 8>(g, stream);
+        case 16: return launch_one<NB, MB, AM, 16>(g, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <SAct AM>
+hipError_t launch_am(const StreamArgs& g, int nb, int mb, int nch, hipStream_t stream) {
+    if (nb == 4) {
+        switch (mb) {
+            case 1: return launch_nch<4, 1, AM>(g, nch, stream);
+            case 2: return launch_nch<4, 2, AM>(g, nch, stream);
+            case 4: return launch_nch<4, 4, AM>(g, nch, stream);
+        }
+    } else if (nb == 2) {
+        switch (mb) {
+            case 1: return launch_nch<2, 1, AM>(g, nch, stream);
+            case 2: return launch_nch<2, 2, AM>(g, nch, stream);
+            case 4: return launch_nch<2, 4, AM>(g, nch, stream);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Activation register budget per wave (kActBudget): 16 VGPRs per batch
+// block and chunk for 16-bit values, 5 for packed codes (the in-register
+// quantization stages 16 per block and chunk until it has encoded them).
+int stream_max_chunks(SAct am, int mb) {
+    int nch = 1;
+    while (nch * 2 <= 16 && nch * 2 * act_regs(am, mb) <= kActBudget) nch *= 2;
+    return nch;
+}
+
+hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipStream_t stream) {
+    if (g.K % 128 != 0 || g.krange % 128 != 0 || g.krange <= 0 || g.ksplit < 1) return hipErrorInvalidValue;
+    if (g.M < 1 || g.M > 16 * mb) return hipErrorInvalidValue;
+    const int64_t chunks = (g.krange + kChunkK - 1) / kChunkK;
+    int nch = 1;
+    while (nch < chunks) nch *= 2;
+    if (nch > stream_max_chunks(am, mb)) return hipErrorInvalidValue;
+    switch (am) {
+        case SAct::kBf16: return launch_am<SAct::kBf16>(g, nb, mb, nch, stream);
+        case SAct::kF16: return launch_am<SAct::kF16>(g, nb, mb, nch, stream);
+        case SAct::kPacked: return launch_am<SAct::kPacked>(g, nb, mb, nch, stream);
+        case SAct::kQuant: return launch_am<SAct::kQuant>(g, nb, mb, nch, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

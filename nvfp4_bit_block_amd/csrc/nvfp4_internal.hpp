@@ -189,6 +189,37 @@ hipError_t launch_lora_a(const uint16_t* x, int64_t rows, int64_t K, const uint1
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
 
+// ------------------------------------------------------- small-batch stream --
+
+// Activation operand of the weight-streaming GEMM (gemm_stream.hip).
+enum class SAct : int {
+    kBf16 = 0,    // bf16 [M, K] (W4A16; weights decoded to bf16 q * s)
+    kF16 = 1,     // f16 [M, K]: the exact products q * s of an NVFP4 activation
+    kPacked = 2,  // NVFP4 codes [M, K/2] + E4M3 scale bytes [M, K/16]
+    kQuant = 3,   // bf16 [M, K], quantized in registers under *a_global (static)
+};
+
+struct StreamArgs {
+    const void* a = nullptr;            // see SAct
+    const uint8_t* a_scales = nullptr;  // kPacked: scale bytes [M, K/16]
+    const float* a_global = nullptr;    // activation global scale (kQuant: the static input scale); null = 1
+    const uint8_t* b_codes = nullptr;   // weight NVFP4 [N, K]
+    const uint8_t* b_scales = nullptr;
+    const float* b_global = nullptr;
+    int64_t M = 0, N = 0, K = 0;
+    int32_t ksplit = 1;                 // K ranges of krange (the last may be shorter)
+    int64_t krange = 0;                 // a multiple of 128
+    void* out = nullptr;                // ksplit 1: bf16 Y [M, N]; else fp32 partials [ksplit, M, N]
+};
+
+// Y = A W^T for 1 <= M <= 16 mb on a grid of ceil(N / (16 nb)) x ksplit
+// workgroups of 8 waves, nb in {2, 4}, mb in {1, 2, 4}; K % 128 == 0 and
+// N * K / 2 < 2^31.  Each K range may hold at most stream_max_chunks(am, mb)
+// chunks of 1024 (rounded up to a power of two); hipErrorInvalidValue
+// otherwise.
+int stream_max_chunks(SAct am, int mb);
+hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipStream_t stream);
+
 // --------------------------------------------------------------------- MoE --
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t slots, int32_t E, int32_t bm,
