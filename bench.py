@@ -633,6 +633,12 @@ def main():
                     "bytes_per_launch": 6144 * 16384 // 2 + 6144 * 16384 // 16,
                     "us_per_launch": head["us_per_launch"]}
     progress("timed steps done")
+    ceil = measure_ceilings(torch, dev, stream, sleeper)
+    if roofline is not None:
+        roofline["ceiling"] = ceil
+        roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / ceil["copy_1GiB_GB_s"], 4)
+        roofline["frac_of_same_size_read_ceiling"] = round(roofline["achieved"] / ceil["read_56.6MB_GB_s"], 4)
+    progress("ceilings measured")
     cpu = None
     if not args.no_cpu_baseline:
         host = {}
@@ -655,9 +661,49 @@ def main():
                                "W4A4 (bf16 and pre-packed activation) and W4A16 GEMM M=1..4096 on both, MoE T=4096 E=256 top-8 H=6144 I=2048",
                    "gpu": torch.cuda.get_device_name(0), "setup_s": round(setup_s, 1),
                    "timing": "HIP events around back-to-back launches enqueued behind a prefill kernel"},
-        "roofline": roofline, "cpu_baseline": cpu, "rows": report,
+        "roofline": roofline, "cpu_baseline": cpu, "hbm_ceiling": ceil, "rows": report,
     }
     print(json.dumps(line))
+
+
+def measure_ceilings(torch, dev, stream, sleeper):
+    """HBM ceilings measured in the same run: a plain device copy of 1 GiB
+    (bytes read + written per second) and a streaming read of the batch-1
+    o_proj GEMV's size (56,623,104 bytes, one reduction launch per buffer,
+    ten buffers in turn so each launch reads HBM rather than the last-level
+    cache), the same-size ceiling of the headline kernel."""
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        if sleeper.ok:
+            torch.cuda._sleep(sleeper.cycles)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda i=0: dst.copy_(src), 10)
+    out["copy_1GiB_GB_s"] = round(2 * n / t / 1e9, 1)
+    del src, dst
+    nb = 6144 * 16384 // 2 + 6144 * 16384 // 16
+    bufs = [torch.ones(nb // 4, dtype=torch.int32, device=dev) for _ in range(10)]
+    res = torch.empty((), dtype=torch.int32, device=dev)
+    t = timed(lambda i=0: torch.amax(bufs[i % 10], dim=0, out=res), 100)
+    out["read_56.6MB_GB_s"] = round(nb / t / 1e9, 1)
+    out["read_56.6MB_us"] = round(t * 1e6, 3)
+    out["note"] = ("ceilings of plain torch kernels on this GPU: device copy_ of 1 GiB; amax over a 56.6 MB "
+                   "int32 buffer (the headline GEMV's bytes), ten buffers rotated, back-to-back launches")
+    del bufs
+    return out
 
 
 class _Sleeper:

@@ -2,6 +2,7 @@
 // host, workspace layout, and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 
@@ -50,7 +51,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     // per row (19 us at M = 4, 31 us at M = 8) while the 32-row tile with its
     // scale preload costs about 26 us at any M up to 32, so the tile takes
     // M >= 7 there (M = 8: W4A4 35.6 -> 26.0 us, W4A16 31.5 -> 26.3 us).
-    if (M <= 4 || (M <= 8 && K <= 4096) || (M <= 6 && K == 16384)) {
+    if (M <= 4 || (M <= 8 && K <= 4096) || (M <= 6 && K > 4096)) {
         p.gemv = true;
         return p;
     }
@@ -175,11 +176,12 @@ GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
     GemmLayout l;
     const GemmPlan p = plan_gemm(M, N, K);
     const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
+    const StreamPlan sq = plan_stream(M, N, K, SAct::kQuant);
     size_t off = 0;
     l.xhat = off; off += align_up((size_t)(M * K * 2));
     size_t part = 0;
-    if (sp.use) {
-        part = stream_partial_bytes(sp, M, N);
+    if (sp.use || sq.use) {
+        part = std::max(stream_partial_bytes(sp, M, N), stream_partial_bytes(sq, M, N));
     } else if (!p.gemv && p.ksplit > 1) {
         part = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
     }
@@ -485,6 +487,16 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     if (!workspace || workspace_bytes < l.total)
         return fail(NVFP4_ERR_WORKSPACE, "gemm: workspace smaller than nvfp4_gemm_w4a4_workspace_size%s");
     hipStream_t s = as_stream(stream);
+    // Up to M = 16 on short rows the stream kernel quantizes the activation
+    // in registers, one launch (measured on MI355X, q_b_proj 16384 x 2048:
+    // M = 8 12.1 -> 10.2 us, M = 16 12.1 -> 11.0 us against the separate
+    // quantize launch); beyond that the redundant encode in every workgroup
+    // costs more than that launch (M = 32 15.1 against 13.8 us).
+    const StreamPlan sq = plan_stream(M, N, K, SAct::kQuant);
+    if (sq.use && M <= 16 && K <= 4096)
+        return hip_status(run_stream(sq, SAct::kQuant, x, nullptr, input_scale, M, N, K, w_codes, w_scales, w_global,
+                                     y, sq.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
+                          "gemm stream");
     const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
     if (sp.use) {
         // the static quantize writes the packed activation (codes, then scale

@@ -17,8 +17,8 @@
 //     scales), in chunks of 1024 K through an NS-stage ring, NS - 1 chunks
 //     in flight;
 //   * the activation slice a wave needs for the whole K range is loaded into
-//     registers once, before the weights (so the ring's vmcnt waits never
-//     wait on it): as 16-bit values (bf16 for W4A16, or the f16 products
+//     registers once, in the prologue (so the ring's vmcnt waits never wait
+//     on it): as 16-bit values (bf16 for W4A16, or the f16 products
 //     q * s of an already quantized activation), as packed NVFP4 codes and
 //     scale bytes decoded to exact f16 q * s at use, or as bf16 values that
 //     the wave quantizes in registers under the static input scale with the
@@ -147,9 +147,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             lds_load4(rb_s, v, 0u, base + (uint32_t)(CODE_BYTES + q * 256));
         }
     };
+    if constexpr (AM != SAct::kQuant) {
 #pragma unroll
-    for (int s = 0; s + 1 < NS; ++s)
-        if (s < nchunks) issue(s, s);
+        for (int s = 0; s + 1 < NS; ++s)
+            if (s < nchunks) issue(s, s);
+    }
 
     // ---- 2. activation loads: this wave's 128-K unit of every chunk, rows
     // 16 mb + i16, as unconditional buffer loads (zeros past M or past the K
@@ -196,9 +198,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    // ---- 3. in-register quantization (kQuant): each lane encodes its two
-    // 16-element blocks per unit under the static scale
+    // ---- 3. in-register quantization (kQuant): the weights are issued only
+    // now (the activation has landed), so the encode runs while they
+    // stream; each lane encodes its two 16-element blocks per unit under the
+    // static scale
     if constexpr (AM == SAct::kQuant) {
+#pragma unroll
+        for (int s = 0; s + 1 < NS; ++s)
+            if (s < nchunks) issue(s, s);
         const float sg = *g.a_global, t = 6.0f * sg;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
@@ -214,6 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
                 xc[c][mb] = make_uint4(c0.x, c0.y, c1.x, c1.y);
                 xs[c][mb] = s2;
             }
+        wait_stages<L>(min(NS - 2, nchunks - 1));
     }
     __syncthreads();
 

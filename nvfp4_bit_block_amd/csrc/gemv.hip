@@ -15,10 +15,10 @@
 //     conversion (one instruction per two elements) and multiplied with the
 //     activation by v_dot2_f32_bf16, one fp32 partial per 16-element block,
 //     scaled once per block;
-//   * the activation is read once per workgroup: k_gemv (the K = 2048 and
-//     K = 16384 layouts) holds each lane's slice of it in VGPRs for every
-//     M <= 8; k_gemv_any (other K) stages it in LDS when M * K * 2 <= 64 KB
-//     and reads it from global memory otherwise;
+//   * the activation is read once per workgroup: k_gemv (the fixed layouts,
+//     K = 2048 times 1, 2, 4, 8 or 16) holds each lane's slice of it in VGPRs
+//     for every M <= 8; k_gemv_any (other K) stages it in LDS when
+//     M * K * 2 <= 64 KB and reads it from global memory otherwise;
 //   * row sums are reduced across the wave with cross-lane shuffles.
 // Weights are read with non-temporal loads: each byte is used once.
 #include "nvfp4_device.hpp"
@@ -361,13 +361,22 @@ hipError_t launch_m(const uint16_t* x, int64_t N, int64_t K, const uint8_t* wc, 
                     const float* g0, const float* g1, uint16_t* y, hipStream_t stream,
                     const uint8_t* xs = nullptr) {
     const bool fits_lds = (int64_t)M * K * 2 <= kMaxLdsBytes;
-    // measured on MI355X (o_proj 6144 x 16384 and q_b_proj 16384 x 2048):
-    // K = 2048: one wave per row, four rows in flight, three workgroups per
-    // CU (two for M > 4); K = 16384: eight waves split K (one 32-element
-    // chunk per lane), four rows in flight, one 512-thread workgroup per CU
-    if (K == 2048)
-        return launch_cfg<M, 1, 1, 4, kThreads, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2, xs);
-    if (K == 16384) return launch_cfg<M, 1, 8, 4, 512, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 1, xs);
+    // K = 2048 KS: KS waves split a row, each lane owning one 32-element
+    // chunk per batch row, four rows in flight per wave.  Measured on MI355X
+    // (o_proj 6144 x 16384 and q_b_proj 16384 x 2048): K = 2048, one wave per
+    // row, three workgroups per CU (two for M > 4); K = 16384, eight waves
+    // per row in one 512-thread workgroup per CU.  The other multiples take
+    // the nearest of these arrangements.
+    if (K % 2048 == 0) {
+        switch (K / 2048) {
+            case 1: return launch_cfg<M, 1, 1, 4, kThreads, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, M <= 4 ? 3 : 2, xs);
+            case 2: return launch_cfg<M, 1, 2, 4, kThreads, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 2, xs);
+            case 4: return launch_cfg<M, 1, 4, 4, 512, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 1, xs);
+            case 8: return launch_cfg<M, 1, 8, 4, 512, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 1, xs);
+            case 16: return launch_cfg<M, 1, 16, 4, 1024, AQ, AP>(x, N, K, wc, ws, g0, g1, y, stream, 1, xs);
+            default: break;
+        }
+    }
     if constexpr (AQ || AP) return hipErrorNotSupported;
     if (fits_lds) return launch_any<M, true>(x, N, K, wc, ws, g0, g1, y, stream);
     return launch_any<M, false>(x, N, K, wc, ws, g0, g1, y, stream);
@@ -401,7 +410,16 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int M, int64_t N, int64_t K, con
 // encodes up front; at M = 1 that hides behind the first weight loads and
 // saves the separate quantize launch, from M = 2 on the two-kernel path is
 // as fast or faster.
-bool gemv_quantizes_activation(int M, int64_t K) { return M == 1 && (K == 2048 || K == 16384); }
+namespace {
+// K of the fixed chunk layouts (2048 times 1, 2, 4, 8 or 16)
+bool fixed_layout(int64_t K) {
+    if (K % 2048 != 0) return false;
+    const int64_t ks = K / 2048;
+    return ks == 1 || ks == 2 || ks == 4 || ks == 8 || ks == 16;
+}
+}  // namespace
+
+bool gemv_quantizes_activation(int M, int64_t K) { return M == 1 && fixed_layout(K); }
 
 hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, const uint8_t* wc,
                             const uint8_t* ws, const float* w_global, const float* input_scale,
@@ -410,9 +428,9 @@ hipError_t launch_gemv_w4a4(const uint16_t* x, int M, int64_t N, int64_t K, cons
     return launch_m<1, true>(x, N, K, wc, ws, w_global, input_scale, y, stream);
 }
 
-// The fixed chunk layouts decode a packed activation in registers; other K
-// expand it to q * s in memory first.
-bool gemv_takes_packed(int M, int64_t K) { return M >= 1 && M <= 8 && (K == 2048 || K == 16384); }
+// The fixed chunk layouts (K = 2048 times 1, 2, 4, 8 or 16) decode a packed
+// activation in registers; other K expand it to q * s in memory first.
+bool gemv_takes_packed(int M, int64_t K) { return M >= 1 && M <= 8 && fixed_layout(K); }
 
 hipError_t launch_gemv_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, int M, int64_t N, int64_t K,
                                    const uint8_t* wc, const uint8_t* ws, const float* w_global,

@@ -79,6 +79,7 @@ __device__ __forceinline__ BlockEnc block_enc(uint32_t max_bits, float Sg, float
 // same quotient and rounding as encode_block.
 __device__ __forceinline__ uint32_t encode_one(uint32_t h, const BlockEnc& b) {
 #pragma clang fp contract(off)
+    if (b.d == 0.0f) return (h >> 12) & 0x8u;   // magnitude 0, the sign remains
     if (b.fast) {
         const float q = div_e2m1(bf16_to_f32(h & 0xFFFFu), b.d, b.y);
         return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, 0.0f, 1.0f, 0) & 0xFu;
@@ -97,6 +98,15 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t w[8], float Sg, 
     const float s_f = (t > 0.0f) ? bmax / t : 0.0f;
     const uint32_t s8 = e4m3_from_f32(s_f);
     const float d = e4m3_to_f32(s8) * Sg;
+    if (d == 0.0f) {
+        // zero divisor (an all-zero block, a zero global scale, or a scale
+        // that rounds to 0): every magnitude code is 0, only the signs remain
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j >> 2] |= (((w[j] >> 12) & 0x08u) | ((w[j] >> 24) & 0x80u)) << (8 * (j & 3));
+        out = make_uint2(o[0], o[1]);
+        return s8;
+    }
     // Fast path when the quotient conditions hold for every element
     // (|x| <= bmax <= 8 d): all blocks of ordinary tensors.  Saturated scales,
     // zero blocks and extreme global scales take the IEEE division.

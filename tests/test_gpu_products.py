@@ -56,13 +56,35 @@ def test_gemv_ragged(orc, N, K):
 
 @pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_gemv_layers_sampled(orc, name, M):
+def test_gemv_layers_full(orc, name, M):
+    # every output of the full-size layer (the oracle takes well under a second)
     w, x, (c0, s0, g0), (c, s, g) = _layer(name)
     xm = x[:M]
     y = host_bf16_f32(nv.gemv_w4a16(dev_bf16(xm), c, s, g))
-    rows = np.sort(np.random.default_rng(M).choice(w.shape[0], 192, replace=False))
-    ref = orc.gemv_w4a16(xm, c0[rows], s0[rows], g0)
-    assert_close(y[:, rows], ref, f"gemv {name} M={M}")
+    assert_close(y, orc.gemv_w4a16(xm, c0, s0, g0), f"gemv {name} M={M}")
+
+
+@pytest.mark.parametrize("K", [4096, 8192, 32768])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_gemv_fixed_layouts(orc, K, M):
+    # the register-resident chunk layouts for K = 2048 times 2, 4 and 16 (the
+    # benchmark layers use 1 and 8): W4A16 at every batch size, the batch-1
+    # W4A4 that quantizes its activation in registers, and the W4A4 on a
+    # pre-packed activation decoded in registers (bit-identical to the
+    # one-call product on the same quantized activation)
+    N = 1000
+    w = wl.layer_weight((N, K), seed=K + M)
+    x = wl.activations(M, K, seed=K + 2 * M)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    y = host_bf16_f32(nv.gemv_w4a16(dev_bf16(x), c, s, g))
+    assert_close(y, orc.gemv_w4a16(x, c0, s0, g0), f"gemv K={K} M={M}")
+    isc = np.float32(orc.global_scale(x))
+    y4 = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    assert_close(y4, orc.gemm_w4a4(x, isc, c0, s0, g0), f"w4a4 K={K} M={M}")
+    ac, asc, ag = nv.quantize(dev_bf16(x), static_scale=float(isc))
+    yp = host_bf16_f32(nv.gemm_w4a4_packed(ac, asc, ag, c, s, g))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(yp.view(np.uint32), y4.view(np.uint32), err_msg=f"packed K={K} M={M}")
 
 
 # -------------------------------------------------------------------- GEMM --
