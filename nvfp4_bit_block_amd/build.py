@@ -64,7 +64,24 @@ def build(jobs: int = 8) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libnvfp4.so failed")
     os.replace(tmp, LIB_PATH)
+    build_probe()
     return LIB_PATH
+
+
+PROBE_SRC = os.path.join(HERE, "probe", "hbm_probe.hip")
+PROBE_PATH = os.path.join(HERE, "libnvfp4_probe.so")
+
+
+def build_probe() -> str:
+    """The benchmark's HBM read-ceiling probe (a separate shared object)."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-x", "hip", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build of libnvfp4_probe.so failed")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 if __name__ == "__main__":
