@@ -43,7 +43,7 @@ struct GemmPlan {
 // 256x256 tile with eight 128x64 waves is the fastest per tile; smaller tiles
 // win where 256x256 leaves most CUs idle; small M streams the weights once
 // and splits K to spread that stream over the chip).
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     GemmPlan p;
     // The VALU GEMV wins while its activation slice fits in registers (M <= 4,
     // the K = 2048 layout up to M = 8) or in LDS (short rows); beyond that the
@@ -56,7 +56,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
         return p;
     }
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-    if (M <= 32) p.tile = A16Tile::k32x256_w32x64;
+    // Short rows with enough tiles for every CU: the thin tiles need no K
+    // split (measured on MI355X, q_b_proj 16384 x 2048: M = 128 on 32 x 256
+    // tiles 19.1 us against 24.0 us for 128 x 128 tiles split in two plus the
+    // split-K pass; M = 256 on the 128 x 128 tile with 32-row waves 26.6
+    // against 28.2 us, f16 activation; with the bf16 activation of W4A16 that
+    // tile loses, 34.2 against 31.5 us)
+    const bool short_k = K <= 4096;
+    if (short_k && M > 64 && M <= 128 && ((M + 31) / 32) * ((N + 255) / 256) >= 256) p.tile = A16Tile::k32x256_w32x64;
+    else if (!bf16_a && short_k && M > 64 && M <= 256 && ((M + 127) / 128) * ((N + 127) / 128) >= 256)
+        p.tile = A16Tile::k128x128_w32x64;
+    else if (M <= 32) p.tile = A16Tile::k32x256_w32x64;
     // 32 < M <= 64: for short K the 128-row tile with 32-row waves (q_b_proj,
     // K = 2048: 22.6 us against 25.4 us with 64 x 256); for long K 64 x 256
     else if (M <= 64) p.tile = K <= 4096 ? A16Tile::k128x128_w32x64 : A16Tile::k64x256_w64x64;
@@ -98,24 +108,46 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 // the row.
 struct StreamPlan {
     bool use = false;
+    SAct am = SAct::kPacked;
     int nb = 4, mb = 1, ksplit = 1;
     int64_t krange = 0;
 };
 
+// For a packed activation above M = 16 the activation is streamed through
+// LDS with the weights (measured on MI355X: q_b_proj M = 32 / 64 10.0 ->
+// 9.0 / 13.7 -> 11.7 us against the activation in registers; o_proj M = 32
+// 27.9 -> 22.8 us and M = 64 36.7 -> 31.3 us against the tiles).
 StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
     StreamPlan p;
     if (M < 1 || M > 64 || N < 1 || K % 128 != 0 || N * (K / 2) >= kMaxOperandBytes || M * K * 2 >= kMaxOperandBytes)
         return p;
     const bool short_k = K <= 4096;
-    if (short_k ? M < 3 : (am == SAct::kBf16 || M < 5 || M > 16)) return p;
+    const bool lds = am == SAct::kPacked && M > 16;
+    if (short_k ? M < 3 : (am == SAct::kBf16 || am == SAct::kQuant || M < 5 || (M > 16 && !lds))) return p;
+    p.am = lds ? SAct::kPackedLds : am;
     p.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    auto krange_of = [&](int s) { return ((K / 128 + s - 1) / s) * 128; };
+    if (lds) {
+        // no register limit on the K range: the widest weight tile first, then
+        // the fewest splits that give at least 192 workgroups
+        for (int nb = 4; nb >= 2; nb -= 2)
+            for (int s = 1; s <= 8 && K / 128 >= s; s *= 2) {
+                if (((N + 16 * nb - 1) / (16 * nb)) * s < 192) continue;
+                p.use = true;
+                p.nb = nb;
+                p.ksplit = s;
+                p.krange = krange_of(s);
+                return p;
+            }
+        return p;
+    }
     const int maxch = stream_max_chunks(am, p.mb);
     // the fewest K splits (partial sums cost an extra pass) that fit the
     // activation registers and give at least 192 workgroups, wider weight
     // tiles first (measured: 192-768 resident workgroups stream alike)
     for (int s = 1; s <= 8; s *= 2) {
         if (K / 128 < s) break;
-        const int64_t krange = ((K / 128 + s - 1) / s) * 128;
+        const int64_t krange = krange_of(s);
         const int64_t chunks = (krange + 1023) / 1024;
         int nch = 1;
         while (nch < chunks) nch *= 2;
@@ -132,7 +164,7 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
     return p;
 }
 
-hipError_t run_stream(const StreamPlan& p, SAct am, const void* a, const uint8_t* a_scales, const float* a_global,
+hipError_t run_stream(const StreamPlan& p, const void* a, const uint8_t* a_scales, const float* a_global,
                       int64_t M, int64_t N, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
                       const float* w_global, uint16_t* y, float* partial, hipStream_t s) {
     StreamArgs g;
@@ -148,7 +180,7 @@ hipError_t run_stream(const StreamPlan& p, SAct am, const void* a, const uint8_t
     g.ksplit = p.ksplit;
     g.krange = p.krange;
     g.out = p.ksplit > 1 ? static_cast<void*>(partial) : static_cast<void*>(y);
-    hipError_t e = launch_gemm_stream(g, am, p.nb, p.mb, s);
+    hipError_t e = launch_gemm_stream(g, p.am, p.nb, p.mb, s);
     if (e != hipSuccess || p.ksplit == 1) return e;
     return launch_splitk_reduce(partial, p.ksplit, M, N, w_global, a_global, y, s);
 }
@@ -197,7 +229,7 @@ GemmLayout layout_gemm(int64_t M, int64_t N, int64_t K) {
 // bf16 operand itself).
 GemmLayout layout_gemm_w4a16(int64_t M, int64_t N, int64_t K) {
     GemmLayout l;
-    const GemmPlan p = plan_gemm(M, N, K);
+    const GemmPlan p = plan_gemm(M, N, K, true);
     const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
     if (sp.use) l.total = stream_partial_bytes(sp, M, N);
     else if (!p.gemv && p.ksplit > 1) l.total = align_up((size_t)p.ksplit * (size_t)(gemm_chunk_rows(M, K) * N) * 4);
@@ -453,7 +485,7 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
     // no workspace)
     const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
     if (sp.use && sp.ksplit == 1)
-        return hip_status(run_stream(sp, SAct::kBf16, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
+        return hip_status(run_stream(sp, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
                                      nullptr, as_stream(stream)),
                           "gemv stream");
     return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y,
@@ -494,7 +526,7 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
     // costs more than that launch (M = 32 15.1 against 13.8 us).
     const StreamPlan sq = plan_stream(M, N, K, SAct::kQuant);
     if (sq.use && M <= 16 && K <= 4096)
-        return hip_status(run_stream(sq, SAct::kQuant, x, nullptr, input_scale, M, N, K, w_codes, w_scales, w_global,
+        return hip_status(run_stream(sq, x, nullptr, input_scale, M, N, K, w_codes, w_scales, w_global,
                                      y, sq.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
                           "gemm stream");
     const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
@@ -513,7 +545,7 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
         a.scales = as;
         int32_t st = hip_status(launch_quantize_pack(a, s), "gemm activation quantize");
         if (st) return st;
-        return hip_status(run_stream(sp, SAct::kPacked, ac, as, input_scale, M, N, K, w_codes, w_scales, w_global, y,
+        return hip_status(run_stream(sp, ac, as, input_scale, M, N, K, w_codes, w_scales, w_global, y,
                                      sp.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
                           "gemm stream");
     }
@@ -570,7 +602,7 @@ int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, 
     hipStream_t s = as_stream(stream);
     const StreamPlan sp = plan_stream(M, N, K, SAct::kPacked);
     if (sp.use)
-        return hip_status(run_stream(sp, SAct::kPacked, a_codes, a_scales, a_global, M, N, K, w_codes, w_scales,
+        return hip_status(run_stream(sp, a_codes, a_scales, a_global, M, N, K, w_codes, w_scales,
                                      w_global, y, sp.ksplit > 1 ? at<float>(workspace, l.partial) : nullptr, s),
                           "gemm_packed stream");
     const GemmPlan p = plan_gemm(M, N, K);
@@ -606,7 +638,7 @@ int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
     if (M < 0 || N < 0 || K <= 0 || K % 16 != 0)
         return fail(NVFP4_ERR_SHAPE, "gemm_w4a16: need M, N >= 0, K > 0 and K %% 16 == 0%s");
     if (K % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "gemm_w4a16: K must be a multiple of 64%s");
-    if (!plan_gemm(M, N, K).gemv && ((int64_t)N * (K / 2) >= kMaxOperandBytes || gemm_chunk_rows(M, K) < 1))
+    if (!plan_gemm(M, N, K, true).gemv && ((int64_t)N * (K / 2) >= kMaxOperandBytes || gemm_chunk_rows(M, K) < 1))
         return fail(NVFP4_ERR_UNSUPPORTED, "gemm_w4a16: weight matrix of 2 GiB or more%s");
     if (M == 0 || N == 0) return NVFP4_OK;
     if (!x || !w_codes || !w_scales || !w_global || !y)
@@ -620,10 +652,10 @@ int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
     hipStream_t s = as_stream(stream);
     const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
     if (sp.use)
-        return hip_status(run_stream(sp, SAct::kBf16, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
+        return hip_status(run_stream(sp, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,
                                      sp.ksplit > 1 ? static_cast<float*>(workspace) : nullptr, s),
                           "gemm_w4a16 stream");
-    const GemmPlan p = plan_gemm(M, N, K);
+    const GemmPlan p = plan_gemm(M, N, K, true);
     if (p.gemv)
         return hip_status(launch_gemv_w4a16(x, (int)M, N, K, w_codes, w_scales, w_global, nullptr, y, s),
                           "gemm_w4a16 gemv");

@@ -93,14 +93,19 @@ __device__ __forceinline__ void wait_stages(int n) {
 template <int NB, int MB, SAct AM, int NS, int NCH>
 __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     using Op = typename std::conditional<AM == SAct::kBf16, bf16x8, f16x8>::type;
-    constexpr bool kPk = AM == SAct::kPacked || AM == SAct::kQuant;   // activation kept packed
-    constexpr int BN = 16 * NB;
-    constexpr int CODE_BYTES = BN * 512, STAGE = BN * (512 + 64);
-    constexpr int LC = BN / 16, LS = BN / 32, L = LC + LS;   // DMA loads per wave per stage
+    constexpr bool kPk = AM == SAct::kPacked || AM == SAct::kQuant;   // activation kept packed in registers
+    constexpr bool kLds = AM == SAct::kPackedLds;                     // packed activation streamed through LDS
+    constexpr int BN = 16 * NB, MP = kLds ? 16 * MB : 0;
+    constexpr int CODE_BYTES = BN * 512, WBYTES = BN * 576;
+    constexpr int ACODE = WBYTES, ASCALE = WBYTES + MP * 512;         // activation rows of a stage (kLds)
+    constexpr int STAGE = WBYTES + MP * 576;
+    constexpr int LC = BN / 16, LS = BN / 32, LCA = MP / 16, LSA = MP / 32;
+    constexpr int L = LC + LS + LCA + LSA;                    // DMA loads per wave per stage
     constexpr int ROWS = 16 * MB, RSTR = BN + 4;             // reduction buffer [wave][row][RSTR] fp32
     constexpr int RED_BYTES = kWaves * ROWS * RSTR * 4;
     constexpr int LDS = NS * STAGE > RED_BYTES ? NS * STAGE : RED_BYTES;
     static_assert(NB == 2 || NB == 4, "whole DMA loads per wave");
+    static_assert(!kLds || MB >= 2, "whole activation DMA loads per wave");
     static_assert(NS >= 2 && NS <= 5 && LDS <= 160 * 1024, "LDS");
     static_assert(L * (NS - 2) <= 63, "vmcnt");
     __shared__ __align__(1024) uint8_t smem[LDS];
@@ -119,6 +124,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);
     const u32x4 rb_c = make_rsrc(g.b_codes, (uint64_t)N * KB);
     const u32x4 rb_s = make_rsrc(g.b_scales, (uint64_t)N * KS);
+    const u32x4 ra_c = make_rsrc(kLds ? g.a : nullptr, kLds ? (uint64_t)M * KB : 0);
+    const u32x4 ra_s = make_rsrc(kLds ? g.a_scales : nullptr, kLds ? (uint64_t)M * KS : 0);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
 
     // ---- 1. the first NS - 1 chunks of weights into the ring
@@ -146,6 +153,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             const uint32_t v = (n < N && kk < k1) ? (uint32_t)n * KS + (uint32_t)(kk / 16) : kOob;
             lds_load4(rb_s, v, 0u, base + (uint32_t)(CODE_BYTES + q * 256));
         }
+        if constexpr (kLds) {
+            // the chunk's activation rows, laid out like the weight rows
+#pragma unroll
+            for (int u = 0; u < LCA; ++u) {
+                const int q = w * LCA + u, r = 2 * q + (lane >> 5);
+                const int unit = (lane & 31) ^ (r & 7);
+                const int64_t kk = kc + 32 * unit;
+                const uint32_t v = (r < M && kk < k1) ? (uint32_t)r * KB + (uint32_t)(kk / 2) : kOob;
+                lds_load16(ra_c, v, 0u, base + (uint32_t)(ACODE + q * 1024));
+            }
+#pragma unroll
+            for (int u = 0; u < LSA; ++u) {
+                const int q = w * LSA + u, r = 4 * q + (lane >> 4);
+                const int d = (lane & 15) ^ (r & 15);
+                const int64_t kk = kc + 64 * d;
+                const uint32_t v = (r < M && kk < k1) ? (uint32_t)r * KS + (uint32_t)(kk / 16) : kOob;
+                lds_load4(ra_s, v, 0u, base + (uint32_t)(ASCALE + q * 256));
+            }
+        }
     };
     if constexpr (AM != SAct::kQuant) {
 #pragma unroll
@@ -159,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     // tracks these loads but not the asm weight loads, so the first use of
     // the activation has to follow a full wait; from here on the K loop
     // issues weight loads only and waits for them itself.)
-    constexpr int XN = kPk ? 1 : NCH, XM = kPk ? 1 : MB;
+    constexpr int XN = (kPk || kLds) ? 1 : NCH, XM = (kPk || kLds) ? 1 : MB;
     constexpr int QN = AM == SAct::kQuant ? NCH : 1, QM = AM == SAct::kQuant ? MB : 1;
     constexpr int PN = kPk ? NCH : 1, PM = kPk ? MB : 1;
     uint4 xa[XN][XM][4];      // 16-bit activation values (kBf16, kF16)
@@ -171,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(g.a_scales), (short)0, (int)(AM == SAct::kPacked ? M * K / 16 : 0), (int)kRsrcWord3);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < (kLds ? 0 : NCH); ++c) {
         const int64_t ku = k0 + (int64_t)c * kChunkK + 128 * w;     // the wave's unit (uniform)
         const bool kin = c < nchunks && ku < k1;
         const int64_t ka = ku + 32 * grp;
@@ -196,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             }
         }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if constexpr (kLds) wait_stages<L>(min(NS - 2, nchunks - 1));   // chunk 0 only: all loads are DMA
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     // ---- 3. in-register quantization (kQuant): the weights are issued only
     // now (the activation has landed), so the encode runs while they
@@ -244,9 +271,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             sw[nb] = e4m3x2_to_f32(*reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * 64));
         }
         f32x2 xsc[MB];
+        uint4 xl[kLds ? MB : 1];
         if constexpr (kPk) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
+        }
+        if constexpr (kLds) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                xl[mb] = *reinterpret_cast<const uint4*>(sb + ACODE + fcode + mb * 16 * 512);
+                xsc[mb] = e4m3x2_to_f32(
+                    *reinterpret_cast<const uint16_t*>(sb + ASCALE + (fscale - CODE_BYTES) + mb * 16 * 64));
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -254,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
+                else if constexpr (kLds) bx[mb] = fp4x8_scaled_f16(word4(xl[mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
                 else bx[mb] = __builtin_bit_cast(Op, xa[c][mb][kk]);
             }
 #pragma unroll
@@ -265,18 +302,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
         }
     };
 
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        if (c < nchunks) {
-            // refill the stage multiplied in iteration c - 1 (all waves passed
-            // the barrier after it)
-            if (c + NS - 1 < nchunks) issue(c + NS - 1, (c + NS - 1) % NS);
-            if (k0 + (int64_t)c * kChunkK + 128 * w < k1) compute(c, c % NS);
-            if (c + 1 < nchunks) {
-                wait_stages<L>(min(NS - 2, nchunks - 2 - c));
-                __syncthreads();
-            }
+    // refill the stage multiplied in iteration c - 1 (all waves passed the
+    // barrier after it), multiply chunk c, wait for chunk c + 1
+    auto iteration = [&](int c, int cr) {
+        if (c + NS - 1 < nchunks) issue(c + NS - 1, (c + NS - 1) % NS);
+        if (k0 + (int64_t)c * kChunkK + 128 * w < k1) compute(cr, c % NS);
+        if (c + 1 < nchunks) {
+            wait_stages<L>(min(NS - 2, nchunks - 2 - c));
+            __syncthreads();
         }
+    };
+    if constexpr (kLds) {
+        // no activation registers to index: a plain loop over any chunk count
+        for (int c = 0; c < nchunks; ++c) iteration(c, 0);
+    } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            if (c < nchunks) iteration(c, c);
     }
 
     // ---- 5. wave partials -> LDS (the ring is free once every wave is here)
@@ -326,14 +368,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 }
 
 constexpr int kActBudget = 128;   // activation VGPRs per wave
-constexpr int act_regs(SAct am, int mb) { return (am == SAct::kPacked ? 5 : 16) * mb; }
+constexpr int act_regs(SAct am, int mb) {
+    return am == SAct::kPackedLds ? 0 : (am == SAct::kPacked ? 5 : 16) * mb;
+}
 
 template <int NB, int MB, SAct AM, int NCH>
 hipError_t launch_one(const StreamArgs& g, hipStream_t stream) {
-    if constexpr (NCH * act_regs(AM, MB) > kActBudget) {
+    if constexpr (NCH * act_regs(AM, MB) > kActBudget || (AM == SAct::kPackedLds && MB < 2)) {
         return hipErrorInvalidValue;
     } else {
-        constexpr int NS = NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
+        // kPackedLds: as many stages (up to four) as LDS holds
+        constexpr int kLdsStage = (16 * NB + 16 * MB) * 576;
+        constexpr int NS = AM == SAct::kPackedLds ? (4 * kLdsStage <= 160 * 1024 ? 4 : 3 * kLdsStage <= 160 * 1024 ? 3 : 2)
+                                                  : NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
         const int64_t ntn = (g.N + 16 * NB - 1) / (16 * NB);
         hipLaunchKernelGGL((k_gemm_stream<NB, MB, AM, NS, NCH>), dim3((unsigned)(ntn * g.ksplit)), dim3(kThreads),
                            0, stream, g);
@@ -377,6 +424,7 @@ hipError_t launch_am(const StreamArgs& g, int nb, int mb, int nch, hipStream_t s
 // block and chunk for 16-bit values, 5 for packed codes (the in-register
 // quantization stages 16 per block and chunk until it has encoded them).
 int stream_max_chunks(SAct am, int mb) {
+    if (am == SAct::kPackedLds) return 1 << 20;   // no activation registers: any chunk count
     int nch = 1;
     while (nch * 2 <= 16 && nch * 2 * act_regs(am, mb) <= kActBudget) nch *= 2;
     return nch;
@@ -389,11 +437,19 @@ hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipS
     int nch = 1;
     while (nch < chunks) nch *= 2;
     if (nch > stream_max_chunks(am, mb)) return hipErrorInvalidValue;
+    if (am == SAct::kPackedLds) {
+        if (nb == 4) return mb == 2 ? launch_one<4, 2, SAct::kPackedLds, 1>(g, stream)
+                          : mb == 4 ? launch_one<4, 4, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
+        if (nb == 2) return mb == 2 ? launch_one<2, 2, SAct::kPackedLds, 1>(g, stream)
+                          : mb == 4 ? launch_one<2, 4, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
+        return hipErrorInvalidValue;
+    }
     switch (am) {
         case SAct::kBf16: return launch_am<SAct::kBf16>(g, nb, mb, nch, stream);
         case SAct::kF16: return launch_am<SAct::kF16>(g, nb, mb, nch, stream);
         case SAct::kPacked: return launch_am<SAct::kPacked>(g, nb, mb, nch, stream);
         case SAct::kQuant: return launch_am<SAct::kQuant>(g, nb, mb, nch, stream);
+        default: break;
     }
     return hipErrorInvalidValue;
 }

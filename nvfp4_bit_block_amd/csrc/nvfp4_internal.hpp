@@ -197,6 +197,7 @@ enum class SAct : int {
     kF16 = 1,     // f16 [M, K]: the exact products q * s of an NVFP4 activation
     kPacked = 2,  // NVFP4 codes [M, K/2] + E4M3 scale bytes [M, K/16]
     kQuant = 3,   // bf16 [M, K], quantized in registers under *a_global (static)
+    kPackedLds = 4,  // as kPacked, streamed through LDS with the weights (M > 16)
 };
 
 struct StreamArgs {

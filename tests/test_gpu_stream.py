@@ -24,7 +24,7 @@ from tests.test_gpu_products import _quant_both
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(3, 12288, 2048), (17, 12288, 1152), (50, 12290, 640), (64, 12288, 4096), (8, 12288, 2048),
+SHAPES = [(3, 12288, 2048), (17, 12288, 1152), (50, 12290, 640), (64, 12288, 4096), (8, 12288, 2048), (40, 6144, 16384),
           (5, 6144, 16384), (16, 3072, 32768), (33, 12352, 1024)]
 
 
