@@ -283,7 +283,7 @@ hipError_t run_gemm_tiles(const GemmPlan& p, const uint16_t* a, AFmt afmt, const
 constexpr int kMoeBM = 128;
 
 struct MoeLayout {
-    size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0;
+    size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0, route = 0;
     size_t xq = 0, hq = 0, h = 0, y = 0, z13 = 0, z2 = 0, total = 0;
 };
 
@@ -297,6 +297,7 @@ MoeLayout layout_moe(const nvfp4_moe_problem& p, int64_t lora_rank = 0) {
     l.perm = off; off += align_up(S * 4);
     l.inv = off; off += align_up(S * 4);
     l.pos_group = off; off += align_up(S * 4);
+    l.route = off; off += align_up(moe_route_scratch_bytes((int64_t)S, (int32_t)p.E));
     if (p.mode == 1) {
         // the quantized activations as exact f16 products q * s, slot order
         l.xq = off; off += align_up(S * (size_t)p.H * 2);
@@ -743,7 +744,8 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
     int32_t* pos_group = at<int32_t>(workspace, l.pos_group);
     uint16_t* h = at<uint16_t>(workspace, l.h);
     float* Y = at<float>(workspace, l.y);
-    int32_t st = hip_status(launch_moe_route(t->topk_ids, S, E, kMoeBM, row_off, tile_off, perm, inv, pos_group, s),
+    int32_t st = hip_status(launch_moe_route(t->topk_ids, S, E, kMoeBM, row_off, tile_off, perm, inv, pos_group,
+                                             at<int32_t>(workspace, l.route), s),
                             "moe route");
     if (st) return st;
     const int grid_m = (int)((S + kMoeBM - 1) / kMoeBM + E);

@@ -223,9 +223,15 @@ hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipS
 
 // --------------------------------------------------------------------- MoE --
 
+// Routing: per-expert row offsets row_off [E + 1] and bm-row tile offsets
+// tile_off [E + 1], the slot of each expert row perm [slots], the row of each
+// slot inv [slots] (-1 for an id outside [0, E)) and the expert of each row
+// pos_group [slots].  `scratch` holds moe_route_scratch_bytes(slots, E) bytes
+// of per-workgroup counts.  E <= 4096.
+size_t moe_route_scratch_bytes(int64_t slots, int32_t E);
 hipError_t launch_moe_route(const int32_t* ids, int64_t slots, int32_t E, int32_t bm,
                             int32_t* row_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
-                            int32_t* pos_group, hipStream_t stream);
+                            int32_t* pos_group, int32_t* scratch, hipStream_t stream);
 
 hipError_t launch_moe_combine(const float* Y, const int32_t* inv, const float* w, int64_t T,
                               int32_t topk, int64_t H, uint16_t* out, hipStream_t stream);

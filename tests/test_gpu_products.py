@@ -338,3 +338,14 @@ def test_moe_rows_beyond_full_tiles(orc, mode):
                                 a13_scale=dev(a13), a2_scale=dev(a2))
     torch.cuda.synchronize()
     assert_close(host_bf16_f32(y), ref, f"moe skewed routing mode {mode}")
+
+
+def test_moe_many_experts_many_runs(orc):
+    """Routing over several workgroup runs of slots (2400 slots) and more
+    experts than the scan has threads (1100), most experts with a few rows."""
+    T, E, k, H, I = 600, 1100, 4, 64, 64
+    x, ids, wts, cw, gw = _moe_case(orc, T, E, k, H, I, seed=77)
+    ref = orc.moe(x, ids, wts, *cw, mode=0)
+    y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A16)
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), ref, "moe many experts")
