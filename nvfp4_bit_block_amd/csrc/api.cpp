@@ -114,19 +114,30 @@ struct StreamPlan {
 };
 
 // For a packed activation above M = 16 the activation is streamed through
-// LDS with the weights (measured on MI355X: q_b_proj M = 32 / 64 10.0 ->
+// LDS with the weights (M = 65-128 on short rows only) (measured on MI355X: q_b_proj M = 32 / 64 10.0 ->
 // 9.0 / 13.7 -> 11.7 us against the activation in registers; o_proj M = 32
 // 27.9 -> 22.8 us and M = 64 36.7 -> 31.3 us against the tiles).
 StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
     StreamPlan p;
-    if (M < 1 || M > 64 || N < 1 || K % 128 != 0 || N * (K / 2) >= kMaxOperandBytes || M * K * 2 >= kMaxOperandBytes)
+    if (M < 1 || M > 128 || N < 1 || K % 128 != 0 || N * (K / 2) >= kMaxOperandBytes || M * K * 2 >= kMaxOperandBytes)
         return p;
     const bool short_k = K <= 4096;
     const bool lds = am == SAct::kPacked && M > 16;
     if (short_k ? M < 3 : (am == SAct::kBf16 || am == SAct::kQuant || M < 5 || (M > 16 && !lds))) return p;
     p.am = lds ? SAct::kPackedLds : am;
-    p.mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     auto krange_of = [&](int s) { return ((K / 128 + s - 1) / s) * 128; };
+    if (M > 64) {
+        // 65-128 rows (512-K stages): only on short rows with 64-row weight
+        // tiles and no K split (measured on MI355X: q_b_proj M = 96 / 128
+        // 30.6 / 23.6 -> 16.3 / 16.9 us; on o_proj, and with any K split, the
+        // tiles are as fast or faster)
+        if (!lds || !short_k || (N + 63) / 64 < 192) return p;
+        p.use = true;
+        p.nb = 4;
+        p.krange = krange_of(1);
+        return p;
+    }
     if (lds) {
         // no register limit on the K range: the widest weight tile first, then
         // the fewest splits that give at least 192 workgroups

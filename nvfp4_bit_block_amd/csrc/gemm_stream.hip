@@ -1,5 +1,5 @@
 // gemm_stream.hip -- small-batch NVFP4 GEMM that streams the weights:
-// Y [M, N] = A [M, K] * W^T with W NVFP4 [N, K] and M <= 64.
+// Y [M, N] = A [M, K] * W^T with W NVFP4 [N, K] and M <= 128.
 //
 // The weight-streaming regime of the W4A4 batch sweep and of W4A16 at
 // small batch (model card "vroomfondel/glm-5.2-reap-504B-v2-W4A4", "Kernel
@@ -56,7 +56,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kChunkK = 1024;          // K per ring stage: 128 per wave
+constexpr int kChunkK = 1024;          // K per ring stage of the register-activation forms
 
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -89,29 +89,46 @@ __device__ __forceinline__ void wait_stages(int n) {
 
 // NB: 16-row weight blocks per workgroup (2 or 4); MB: 16-row batch blocks
 // (M <= 16 MB); NS: ring stages (2..5); NCH: the most 1024-K chunks a
-// workgroup's K range may hold (sizes the activation registers).
-template <int NB, int MB, SAct AM, int NS, int NCH>
+// workgroup's K range may hold (sizes the activation registers); CK: K per
+// ring stage (1024, or 512 so that up to 128 activation rows fit a stage;
+// kPackedLds only).  The waves split a stage's K into WK = CK / 128 units of
+// 128 and, when WK < 8, the batch blocks into 8 / WK groups.
+template <int NB, int MB, SAct AM, int NS, int NCH, int CK = kChunkK>
 __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     using Op = typename std::conditional<AM == SAct::kBf16, bf16x8, f16x8>::type;
     constexpr bool kPk = AM == SAct::kPacked || AM == SAct::kQuant;   // activation kept packed in registers
     constexpr bool kLds = AM == SAct::kPackedLds;                     // packed activation streamed through LDS
+    static_assert(CK == kChunkK || (kLds && CK == 512), "512-K stages stream the activation");
+    constexpr int WK = CK / 128, WM = kWaves / WK, MBW = MB / WM;
+    constexpr int RC = CK / 2, RSB = CK / 16;                 // code and scale bytes of a row per stage
+    constexpr int NSLOT = RC / 16, NDW = RSB / 4;             // its 16-byte code slots and scale dwords
     constexpr int BN = 16 * NB, MP = kLds ? 16 * MB : 0;
-    constexpr int CODE_BYTES = BN * 512, WBYTES = BN * 576;
-    constexpr int ACODE = WBYTES, ASCALE = WBYTES + MP * 512;         // activation rows of a stage (kLds)
-    constexpr int STAGE = WBYTES + MP * 576;
-    constexpr int LC = BN / 16, LS = BN / 32, LCA = MP / 16, LSA = MP / 32;
+    constexpr int CODE_BYTES = BN * RC, WBYTES = BN * (RC + RSB);
+    constexpr int ACODE = WBYTES, ASCALE = WBYTES + MP * RC;          // activation rows of a stage (kLds)
+    // a load instruction of a wave covers 1 KB of codes (1024 / RC rows) or
+    // 256 bytes of scales (256 / RSB rows); every wave issues the same number
+    // of each kind, and one numbered past the last slab loads zeros into a
+    // 1 KB pad at the end of the stage
+    constexpr int NLC = BN * RC / 1024, NLS = BN * RSB / 256, NLCA = MP * RC / 1024, NLSA = MP * RSB / 256;
+    constexpr int LC = (NLC + kWaves - 1) / kWaves, LS = (NLS + kWaves - 1) / kWaves;
+    constexpr int LCA = (NLCA + kWaves - 1) / kWaves, LSA = (NLSA + kWaves - 1) / kWaves;
+    constexpr bool kPad = LC * kWaves != NLC || LS * kWaves != NLS || LCA * kWaves != NLCA || LSA * kWaves != NLSA;
+    constexpr int PAD = WBYTES + MP * (RC + RSB);
+    constexpr int STAGE = PAD + (kPad ? 1024 : 0);
     constexpr int L = LC + LS + LCA + LSA;                    // DMA loads per wave per stage
-    constexpr int ROWS = 16 * MB, RSTR = BN + 4;             // reduction buffer [wave][row][RSTR] fp32
-    constexpr int RED_BYTES = kWaves * ROWS * RSTR * 4;
+    constexpr int ROWS = 16 * MB, RSTR = BN + 4;             // reduction buffer [K unit][row][RSTR] fp32
+    constexpr int RED_BYTES = WK * ROWS * RSTR * 4;
     constexpr int LDS = NS * STAGE > RED_BYTES ? NS * STAGE : RED_BYTES;
-    static_assert(NB == 2 || NB == 4, "whole DMA loads per wave");
-    static_assert(!kLds || MB >= 2, "whole activation DMA loads per wave");
+    static_assert(NB == 2 || NB == 4, "weight row blocks");
+    static_assert(!kLds || MB >= 2, "activation row blocks");
+    static_assert(MB % WM == 0, "batch blocks per wave group");
     static_assert(NS >= 2 && NS <= 5 && LDS <= 160 * 1024, "LDS");
     static_assert(L * (NS - 2) <= 63, "vmcnt");
     __shared__ __align__(1024) uint8_t smem[LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = w % WK, wm = w / WK;                       // K unit and batch group of the wave
     const int i16 = lane & 15, grp = lane >> 4;
 
     const int64_t N = g.N, K = g.K, M = g.M;
@@ -120,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const int64_t n0 = (int64_t)tn * BN;
     const int64_t k0 = (int64_t)kz * g.krange;
     const int64_t k1 = min(K, k0 + g.krange);
-    const int nchunks = (int)((k1 - k0 + kChunkK - 1) / kChunkK);   // 1 .. NCH (launcher)
+    const int nchunks = (int)((k1 - k0 + CK - 1) / CK);   // 1 .. NCH (launcher; any count for kLds)
     const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);
     const u32x4 rb_c = make_rsrc(g.b_codes, (uint64_t)N * KB);
     const u32x4 rb_s = make_rsrc(g.b_scales, (uint64_t)N * KS);
@@ -129,48 +146,44 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
 
     // ---- 1. the first NS - 1 chunks of weights into the ring
-    // chunk c into stage st: code load q = w LC + u covers rows 2q, 2q + 1
-    // (lane / 32), slot lane % 32 <- chunk (lane % 32) ^ (row % 8); scale load
-    // q = w LS + u covers rows 4q .. 4q + 3 (lane / 16), dword slot lane % 16
-    // <- dword (lane % 16) ^ (row % 16).  Pieces past N or past the K range
-    // read zeros.
+    // chunk c into stage st: code load q = w LC + u covers rows
+    // (1024 / RC) q + lane / NSLOT, slot lane % NSLOT <- the row's 16-byte
+    // chunk (lane % NSLOT) ^ (row % 8); scale load q covers rows
+    // (256 / RSB) q + lane / NDW, dword slot lane % NDW <- dword
+    // (lane % NDW) ^ (row % NDW).  Pieces past N, M or the K range read zeros.
+    constexpr int RPC = 1024 / RC, RPS = 256 / RSB;
+    // (q and nq are wave-uniform, so is the LDS destination)
+    auto code_load = [&](const u32x4& rs, int q, int nq, int64_t row0, int64_t rows, int64_t kc, uint32_t region,
+                         uint32_t pad) {
+        const int r = RPC * q + lane / NSLOT;
+        const int unit = (lane % NSLOT) ^ (r & 7);
+        const int64_t row = row0 + r, kk = kc + 32 * unit;
+        const bool in = q < nq && row < rows && kk < k1;
+        lds_load16(rs, in ? (uint32_t)row * KB + (uint32_t)(kk / 2) : kOob, 0u,
+                   q < nq ? region + (uint32_t)(q * 1024) : pad);
+    };
+    auto scale_load = [&](const u32x4& rs, int q, int nq, int64_t row0, int64_t rows, int64_t kc, uint32_t region,
+                          uint32_t pad) {
+        const int r = RPS * q + lane / NDW;
+        const int d = (lane % NDW) ^ (r & (NDW - 1));
+        const int64_t row = row0 + r, kk = kc + 64 * d;
+        const bool in = q < nq && row < rows && kk < k1;
+        lds_load4(rs, in ? (uint32_t)row * KS + (uint32_t)(kk / 16) : kOob, 0u,
+                  q < nq ? region + (uint32_t)(q * 256) : pad);
+    };
     auto issue = [&](int c, int st) {
-        const uint32_t base = lds0 + (uint32_t)(st * STAGE);
-        const int64_t kc = k0 + (int64_t)c * kChunkK;
+        const uint32_t base = lds0 + (uint32_t)(st * STAGE), pad = base + (uint32_t)PAD;
+        const int64_t kc = k0 + (int64_t)c * CK;
 #pragma unroll
-        for (int u = 0; u < LC; ++u) {
-            const int q = w * LC + u, r = 2 * q + (lane >> 5);
-            const int unit = (lane & 31) ^ (r & 7);
-            const int64_t n = n0 + r, kk = kc + 32 * unit;
-            const uint32_t v = (n < N && kk < k1) ? (uint32_t)n * KB + (uint32_t)(kk / 2) : kOob;
-            lds_load16(rb_c, v, 0u, base + (uint32_t)(q * 1024));
-        }
+        for (int u = 0; u < LC; ++u) code_load(rb_c, w * LC + u, NLC, n0, N, kc, base, pad);
 #pragma unroll
-        for (int u = 0; u < LS; ++u) {
-            const int q = w * LS + u, r = 4 * q + (lane >> 4);
-            const int d = (lane & 15) ^ (r & 15);
-            const int64_t n = n0 + r, kk = kc + 64 * d;
-            const uint32_t v = (n < N && kk < k1) ? (uint32_t)n * KS + (uint32_t)(kk / 16) : kOob;
-            lds_load4(rb_s, v, 0u, base + (uint32_t)(CODE_BYTES + q * 256));
-        }
+        for (int u = 0; u < LS; ++u) scale_load(rb_s, w * LS + u, NLS, n0, N, kc, base + (uint32_t)CODE_BYTES, pad);
         if constexpr (kLds) {
             // the chunk's activation rows, laid out like the weight rows
 #pragma unroll
-            for (int u = 0; u < LCA; ++u) {
-                const int q = w * LCA + u, r = 2 * q + (lane >> 5);
-                const int unit = (lane & 31) ^ (r & 7);
-                const int64_t kk = kc + 32 * unit;
-                const uint32_t v = (r < M && kk < k1) ? (uint32_t)r * KB + (uint32_t)(kk / 2) : kOob;
-                lds_load16(ra_c, v, 0u, base + (uint32_t)(ACODE + q * 1024));
-            }
+            for (int u = 0; u < LCA; ++u) code_load(ra_c, w * LCA + u, NLCA, 0, M, kc, base + (uint32_t)ACODE, pad);
 #pragma unroll
-            for (int u = 0; u < LSA; ++u) {
-                const int q = w * LSA + u, r = 4 * q + (lane >> 4);
-                const int d = (lane & 15) ^ (r & 15);
-                const int64_t kk = kc + 64 * d;
-                const uint32_t v = (r < M && kk < k1) ? (uint32_t)r * KS + (uint32_t)(kk / 16) : kOob;
-                lds_load4(ra_s, v, 0u, base + (uint32_t)(ASCALE + q * 256));
-            }
+            for (int u = 0; u < LSA; ++u) scale_load(ra_s, w * LSA + u, NLSA, 0, M, kc, base + (uint32_t)ASCALE, pad);
         }
     };
     if constexpr (AM != SAct::kQuant) {
@@ -253,42 +266,46 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     __syncthreads();
 
     // ---- 4. the K loop
-    f32x4 acc[NB][MB];
+    f32x4 acc[NB][MBW];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t fcode = (uint32_t)(i16 * 512 + 16 * ((4 * w + grp) ^ (i16 & 7)));
-    const uint32_t fscale = (uint32_t)(CODE_BYTES + i16 * 64 + 4 * ((2 * w + (grp >> 1)) ^ i16) + 2 * (grp & 1));
+        for (int mb = 0; mb < MBW; ++mb) acc[nb][mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t fcode = (uint32_t)(i16 * RC + 16 * ((4 * wk + grp) ^ (i16 & 7)));
+    const uint32_t fscale =
+        (uint32_t)(CODE_BYTES + i16 * RSB + 4 * ((2 * wk + (grp >> 1)) ^ (i16 & (NDW - 1))) + 2 * (grp & 1));
 
+    // (the wave's batch blocks are wm MBW .. wm MBW + MBW - 1; with the
+    // activation in registers WM = 1 and they are all MB)
     auto compute = [&](int c, int st) {
         const uint8_t* sb = smem + st * STAGE;
         uint4 cw[NB];
         f32x2 sw[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            cw[nb] = *reinterpret_cast<const uint4*>(sb + fcode + nb * 16 * 512);
-            sw[nb] = e4m3x2_to_f32(*reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * 64));
+            cw[nb] = *reinterpret_cast<const uint4*>(sb + fcode + nb * 16 * RC);
+            sw[nb] = e4m3x2_to_f32(*reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * RSB));
         }
-        f32x2 xsc[MB];
-        uint4 xl[kLds ? MB : 1];
+        f32x2 xsc[MBW];
+        uint4 xl[kLds ? MBW : 1];
         if constexpr (kPk) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
+            for (int mb = 0; mb < MBW; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
         }
         if constexpr (kLds) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                xl[mb] = *reinterpret_cast<const uint4*>(sb + ACODE + fcode + mb * 16 * 512);
+            for (int mb = 0; mb < MBW; ++mb) {
+                const int b = wm * MBW + mb;
+                xl[mb] = *reinterpret_cast<const uint4*>(sb + ACODE + fcode + b * 16 * RC);
                 xsc[mb] = e4m3x2_to_f32(
-                    *reinterpret_cast<const uint16_t*>(sb + ASCALE + (fscale - CODE_BYTES) + mb * 16 * 64));
+                    *reinterpret_cast<const uint16_t*>(sb + ASCALE + (fscale - CODE_BYTES) + b * 16 * RSB));
             }
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            Op bx[MB];
+            Op bx[MBW];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
+            for (int mb = 0; mb < MBW; ++mb) {
                 if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
                 else if constexpr (kLds) bx[mb] = fp4x8_scaled_f16(word4(xl[mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
                 else bx[mb] = __builtin_bit_cast(Op, xa[c][mb][kk]);
@@ -297,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             for (int nb = 0; nb < NB; ++nb) {
                 const Op av = decode8(word4(cw[nb], kk), kk < 2 ? sw[nb].x : sw[nb].y, (Op*)nullptr);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16(av, bx[mb], acc[nb][mb]);
+                for (int mb = 0; mb < MBW; ++mb) acc[nb][mb] = mfma16(av, bx[mb], acc[nb][mb]);
             }
         }
     };
@@ -306,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     // barrier after it), multiply chunk c, wait for chunk c + 1
     auto iteration = [&](int c, int cr) {
         if (c + NS - 1 < nchunks) issue(c + NS - 1, (c + NS - 1) % NS);
-        if (k0 + (int64_t)c * kChunkK + 128 * w < k1) compute(cr, c % NS);
+        if (k0 + (int64_t)c * CK + 128 * wk < k1) compute(cr, c % NS);
         if (c + 1 < nchunks) {
             wait_stages<L>(min(NS - 2, nchunks - 2 - c));
             __syncthreads();
@@ -321,17 +338,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             if (c < nchunks) iteration(c, c);
     }
 
-    // ---- 5. wave partials -> LDS (the ring is free once every wave is here)
+    // ---- 5. wave partials -> LDS (the ring is free once every wave is here),
+    // one plane per K unit
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            *reinterpret_cast<f32x4*>(red + (w * ROWS + 16 * mb + i16) * RSTR + 16 * nb + 4 * grp) = acc[nb][mb];
+        for (int mb = 0; mb < MBW; ++mb)
+            *reinterpret_cast<f32x4*>(red + (wk * ROWS + 16 * (wm * MBW + mb) + i16) * RSTR + 16 * nb + 4 * grp) =
+                acc[nb][mb];
     __syncthreads();
 
-    // ---- 6. sum in wave order; thread e takes batch row e / (BN/4) and four
+    // ---- 6. sum in K-unit order; thread e takes batch row e / (BN/4) and four
     // consecutive weight rows
     constexpr int NG = BN / 4;
     const float scale = (g.a_global ? *g.a_global : 1.0f) * *g.b_global;
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
         const int mr = e / NG, ng = e - mr * NG;
         f32x4 s = *reinterpret_cast<const f32x4*>(red + mr * RSTR + 4 * ng);
 #pragma unroll
-        for (int v = 1; v < kWaves; ++v) s += *reinterpret_cast<const f32x4*>(red + (v * ROWS + mr) * RSTR + 4 * ng);
+        for (int v = 1; v < WK; ++v) s += *reinterpret_cast<const f32x4*>(red + (v * ROWS + mr) * RSTR + 4 * ng);
         const int64_t m = mr, n = n0 + 4 * ng;
         if (m >= M || n >= N) continue;
         if (g.ksplit > 1) {
@@ -372,18 +391,30 @@ constexpr int act_regs(SAct am, int mb) {
     return am == SAct::kPackedLds ? 0 : (am == SAct::kPacked ? 5 : 16) * mb;
 }
 
+// Bytes of one ring stage of the LDS-streamed form (weight and activation
+// rows, and the 1 KB pad when the loads do not divide evenly among the waves).
+template <int NB, int MB, int CK>
+constexpr int lds_stage_bytes() {
+    constexpr int RC = CK / 2, RSB = CK / 16, BN = 16 * NB, MP = 16 * MB;
+    constexpr bool pad = (BN * RC / 1024) % kWaves || (BN * RSB / 256) % kWaves || (MP * RC / 1024) % kWaves ||
+                         (MP * RSB / 256) % kWaves;
+    return (BN + MP) * (RC + RSB) + (pad ? 1024 : 0);
+}
+
 template <int NB, int MB, SAct AM, int NCH>
 hipError_t launch_one(const StreamArgs& g, hipStream_t stream) {
     if constexpr (NCH * act_regs(AM, MB) > kActBudget || (AM == SAct::kPackedLds && MB < 2)) {
         return hipErrorInvalidValue;
     } else {
-        // kPackedLds: as many stages (up to four) as LDS holds
-        constexpr int kLdsStage = (16 * NB + 16 * MB) * 576;
+        // kPackedLds: 512-K stages above 64 batch rows, and as many stages
+        // (up to four) as LDS holds
+        constexpr int CK = AM == SAct::kPackedLds && MB > 4 ? 512 : kChunkK;
+        constexpr int kLdsStage = lds_stage_bytes<NB, MB, CK>();
         constexpr int NS = AM == SAct::kPackedLds ? (4 * kLdsStage <= 160 * 1024 ? 4 : 3 * kLdsStage <= 160 * 1024 ? 3 : 2)
                                                   : NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
         const int64_t ntn = (g.N + 16 * NB - 1) / (16 * NB);
-        hipLaunchKernelGGL((k_gemm_stream<NB, MB, AM, NS, NCH>), dim3((unsigned)(ntn * g.ksplit)), dim3(kThreads),
-                           0, stream, g);
+        hipLaunchKernelGGL((k_gemm_stream<NB, MB, AM, NS, NCH, CK>), dim3((unsigned)(ntn * g.ksplit)),
+                           dim3(kThreads), 0, stream, g);
         return hipGetLastError();
     }
 }
@@ -439,9 +470,11 @@ hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipS
     if (nch > stream_max_chunks(am, mb)) return hipErrorInvalidValue;
     if (am == SAct::kPackedLds) {
         if (nb == 4) return mb == 2 ? launch_one<4, 2, SAct::kPackedLds, 1>(g, stream)
-                          : mb == 4 ? launch_one<4, 4, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
+                          : mb == 4 ? launch_one<4, 4, SAct::kPackedLds, 1>(g, stream)
+                          : mb == 8 ? launch_one<4, 8, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
         if (nb == 2) return mb == 2 ? launch_one<2, 2, SAct::kPackedLds, 1>(g, stream)
-                          : mb == 4 ? launch_one<2, 4, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
+                          : mb == 4 ? launch_one<2, 4, SAct::kPackedLds, 1>(g, stream)
+                          : mb == 8 ? launch_one<2, 8, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
         return hipErrorInvalidValue;
     }
     switch (am) {

@@ -214,7 +214,8 @@ struct StreamArgs {
 };
 
 // Y = A W^T for 1 <= M <= 16 mb on a grid of ceil(N / (16 nb)) x ksplit
-// workgroups of 8 waves, nb in {2, 4}, mb in {1, 2, 4}; K % 128 == 0 and
+// workgroups of 8 waves, nb in {2, 4}, mb in {1, 2, 4} (kPackedLds: 2, 4
+// or 8, the last on 512-K ring stages); K % 128 == 0 and
 // N * K / 2 < 2^31.  Each K range may hold at most stream_max_chunks(am, mb)
 // chunks of 1024 (rounded up to a power of two); hipErrorInvalidValue
 // otherwise.

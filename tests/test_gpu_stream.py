@@ -1,11 +1,13 @@
 """GPU parity of the weight-streaming small-batch GEMM (the planner sends
 W4A4, pre-packed W4A4 and W4A16 products with M <= 64 to it on short rows,
-and pre-packed/one-call W4A4 with M = 5..16 on long rows) against the
+pre-packed/one-call W4A4 with M = 65..128 on short rows (512-K ring stages,
+the waves split into four K units and two batch halves), and
+pre-packed/one-call W4A4 with M = 5..64 on long rows) against the
 oracle, elementwise |y - ref| <= 1e-3 + 1e-2 |ref|, on sampled outputs of
 problems large enough for the planner to pick it (at least 192 workgroups).
 
-The shapes reach the kernel's edges: batch rows that fill 1, 2 and 4 of its
-16-row blocks partly, weight rows that end inside a 64-row tile (and a row
+The shapes reach the kernel's edges: batch rows that fill 1, 2, 4 and 8 of
+its 16-row blocks partly, weight rows that end inside a 64-row tile (and a row
 count that is not a multiple of 4, the scalar-store path), K ranges whose last
 1024-K chunk is partial (some waves idle), and K splits with the split-K
 reduction (bf16 activation at M = 64, K = 4096; packed activation on
@@ -25,7 +27,8 @@ from tests.test_gpu_products import _quant_both
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(3, 12288, 2048), (17, 12288, 1152), (50, 12290, 640), (64, 12288, 4096), (8, 12288, 2048), (40, 6144, 16384),
-          (5, 6144, 16384), (16, 3072, 32768), (33, 12352, 1024)]
+          (5, 6144, 16384), (16, 3072, 32768), (33, 12352, 1024),
+          (65, 12288, 2048), (100, 12290, 1152), (128, 16384, 640), (97, 12352, 4096)]
 
 
 def _sample(M, N, seed):
