@@ -132,8 +132,8 @@ int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const floa
  * of x^T computed from the full-precision x (blocks of 16 along rows, same
  * global scale and block rule as nvfp4_quantize, dynamic or static).
  * x bf16 [rows, cols] -> codes_t [cols, rows/2], scales_t [cols, rows/16],
- * *global_scale.  rows % 16 == 0 (else SHAPE), cols % 8 == 0 (else
- * UNSUPPORTED).  Workspace as nvfp4_quantize: nvfp4_quantize_workspace_size
+ * *global_scale.  rows % 16 == 0 (else SHAPE), cols % 8 == 0 and rows <=
+ * 65535 * 128 (else UNSUPPORTED).  Workspace as nvfp4_quantize: nvfp4_quantize_workspace_size
  * (rows, cols) bytes in dynamic mode, none in static mode.  Bit-identical to
  * nvfp4_quantize of the transposed tensor.
  *
@@ -141,7 +141,8 @@ int32_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const floa
  * dequantized to bf16 and transposed on the fly for a bf16 Dgrad:
  * y_t[c, r] = bf16( fl(fl(q[r, c] * s[r, c/16]) * Sg) ), y_t bf16 [cols, rows]
  * (the transpose of nvfp4_dequantize's output, bit for bit).  cols % 16 == 0
- * (else SHAPE), rows % 8 == 0 (else UNSUPPORTED).  No workspace.
+ * (else SHAPE), rows % 8 == 0 and cols <= 65535 * 128 (else UNSUPPORTED).
+ * No workspace.
  * ------------------------------------------------------------------------ */
 int32_t nvfp4_quantize_columnwise(const uint16_t* x, int64_t rows, int64_t cols, const float* static_scale,
                                   uint8_t* codes_t, uint8_t* scales_t, float* global_scale, void* workspace,

@@ -427,6 +427,8 @@ int32_t nvfp4_quantize_columnwise(const uint16_t* x, int64_t rows, int64_t cols,
     if (rows < 0 || cols < 0 || rows % 16 != 0)
         return fail(NVFP4_ERR_SHAPE, "quantize_columnwise: need rows, cols >= 0 and rows %% 16 == 0%s");
     if (cols % 8 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "quantize_columnwise: cols must be a multiple of 8%s");
+    if ((rows + 127) / 128 > 65535)
+        return fail(NVFP4_ERR_UNSUPPORTED, "quantize_columnwise: at most 65535 x 128 rows%s");
     if (rows == 0 || cols == 0) return NVFP4_OK;
     if (!x || !codes_t || !scales_t || !global_scale)
         return fail(NVFP4_ERR_NULL_ARG, "quantize_columnwise: x, codes, scales and global_scale are required%s");
@@ -456,6 +458,8 @@ int32_t nvfp4_dequantize_transpose(const uint8_t* codes, const uint8_t* scales, 
     if (rows < 0 || cols <= 0 || cols % 16 != 0)
         return fail(NVFP4_ERR_SHAPE, "dequantize_transpose: need rows >= 0, cols > 0 and cols %% 16 == 0%s");
     if (rows % 8 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "dequantize_transpose: rows must be a multiple of 8%s");
+    if ((cols + 127) / 128 > 65535)
+        return fail(NVFP4_ERR_UNSUPPORTED, "dequantize_transpose: at most 65535 x 128 cols%s");
     if (rows == 0) return NVFP4_OK;
     if (!codes || !scales || !global_scale || !y_t)
         return fail(NVFP4_ERR_NULL_ARG, "dequantize_transpose: all pointers are required%s");

@@ -133,7 +133,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint8_t* __restric
                                                         int64_t C, uint16_t* __restrict__ y_t) {
     __shared__ uint32_t tile[kDC * kDStride];
     const float Sg = *sg_ptr;
-    const int64_t r0 = (int64_t)blockIdx.y * kDR, c0 = (int64_t)blockIdx.x * kDC;
+    // blockIdx.x walks the row tiles, so workgroups that run together write
+    // adjacent 256-byte pieces of the same output rows
+    const int64_t r0 = (int64_t)blockIdx.x * kDR, c0 = (int64_t)blockIdx.y * kDC;
     const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
     const int64_t r = r0 + 2 * p, cq = c0 + 32 * q;
     const int64_t bpr = C / 16;
@@ -194,7 +196,7 @@ hipError_t launch_quantize_cols(const uint16_t* x, int64_t rows, int64_t cols, S
 
 hipError_t launch_dequantize_t(const uint8_t* codes, const uint8_t* scales, const float* sg_ptr, int64_t rows,
                                int64_t cols, uint16_t* y_t, hipStream_t stream) {
-    const dim3 grid((unsigned)((cols + kDC - 1) / kDC), (unsigned)((rows + kDR - 1) / kDR));
+    const dim3 grid((unsigned)((rows + kDR - 1) / kDR), (unsigned)((cols + kDC - 1) / kDC));
     hipLaunchKernelGGL(k_dequant_t, grid, dim3(kThreads), 0, stream, codes, scales, sg_ptr, rows, cols, y_t);
     return hipGetLastError();
 }

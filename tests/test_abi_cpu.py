@@ -79,12 +79,14 @@ def test_columnwise_and_transpose_validation():
     assert q(A, 32, 16, None, MIS, A, A, A, 1 << 20, None) == ALIGN
     assert q(A, 32, 16, None, A, A, A, None, 0, None) == WS                  # dynamic needs workspace
     assert q(A, 0, 16, None, A, A, A, None, 0, None) == OK
+    assert q(A, 65536 * 128, 16, None, A, A, A, A, 1 << 40, None) == UNSUP  # row tiles past the grid's y limit
     d = L.nvfp4_dequantize_transpose
     assert d(None, A, A, 8, 32, A, None) == NULL
     assert d(A, A, A, 8, 24, A, None) == SHAPE                               # cols % 16
     assert d(A, A, A, 12, 32, A, None) == UNSUP                              # rows % 8
     assert d(A, A, A, 8, 32, MIS, None) == ALIGN
     assert d(A, A, A, 0, 32, A, None) == OK
+    assert d(A, A, A, 8, 65536 * 128, A, None) == UNSUP                      # column tiles past the grid's y limit
 
 
 def test_gemv_validation():
