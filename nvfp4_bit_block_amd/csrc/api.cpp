@@ -63,6 +63,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     // against 28.2 us, f16 activation; with the bf16 activation of W4A16 that
     // tile loses, 34.2 against 31.5 us)
     const bool short_k = K <= 4096;
+    // Long rows above M = 128: the 256 x 256 tile (its software-pipelined
+    // 128-row waves) with K split until about one workgroup per CU beats the
+    // 128 x 128 tiles (measured on MI355X, o_proj 6144 x 16384, f16 / bf16
+    // activation: M = 256 72.4 / 87.5 -> 69.9 / 74.2 us at split 8; M = 512
+    // 127.2 / 161.6 -> 116.6 / 123.8 at split 4; M = 1024 241.8 / 268.7 ->
+    // 207.7 / 235.9 at split 2; M = 2048 445 -> 419 us unsplit).  On short
+    // rows it needs 192 tiles of its own (q_b_proj M = 512: 128 x 128 tiles
+    // 42.1 us against 55.9).
+    const bool long_wide = !short_k && M > 128;
     if (short_k && M > 64 && M <= 128 && ((M + 31) / 32) * ((N + 255) / 256) >= 256) p.tile = A16Tile::k32x256_w32x64;
     else if (!bf16_a && short_k && M > 64 && M <= 256 && ((M + 127) / 128) * ((N + 127) / 128) >= 256)
         p.tile = A16Tile::k128x128_w32x64;
@@ -70,8 +79,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     // 32 < M <= 64: for short K the 128-row tile with 32-row waves (q_b_proj,
     // K = 2048: 22.6 us against 25.4 us with 64 x 256); for long K 64 x 256
     else if (M <= 64) p.tile = K <= 4096 ? A16Tile::k128x128_w32x64 : A16Tile::k64x256_w64x64;
-    else if (M <= 128 || big < 192) p.tile = A16Tile::k128x128_w64x64;
-    else p.tile = A16Tile::k256x256_w128x64;
+    else if (long_wide || (M > 128 && big >= 192)) p.tile = A16Tile::k256x256_w128x64;
+    else p.tile = A16Tile::k128x128_w64x64;
     const int64_t bm = a16_tile_rows(p.tile), bn = a16_tile_cols(p.tile);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t ksteps = K / 64;
@@ -80,16 +89,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     // (6144 x 16384), 192 workgroups (split 8) beat 384 (split 16) by 7-14 %,
     // each further split adding a partial-sum pass over M x N and a workgroup
     // prologue for the same weight stream
+    // (the 256 x 256 tile on long rows stops at 192 workgroups, one per CU:
+    // M = 256 split 8 69.9 us against split 4 100.1 us; M = 2048 unsplit 419
+    // against split 2 445 us)
+    const bool one_per_cu = long_wide && p.tile == A16Tile::k256x256_w128x64;
     auto wants_split = [&]() {
-        return M <= 64 ? tiles * p.ksplit * 2 <= 256 : tiles * p.ksplit < 256;
+        return M <= 64 ? tiles * p.ksplit * 2 <= 256 : tiles * p.ksplit < (one_per_cu ? 192 : 256);
     };
     while (wants_split() && p.ksplit < 16 && ksteps / (p.ksplit * 2) >= 8) p.ksplit *= 2;
     // 256-511 tiles on long K leave some CUs one tile and others two (o_proj
-    // at M = 1024: 384 tiles of 128 x 128, three workgroups per CU; at
-    // M = 4096: 384 tiles of 256 x 256, one per CU, so 1.5 rounds); split 2
-    // evens the load (M = 1024: W4A4 246.6 -> 234.2 us, W4A16 267.8 -> 242.1;
-    // M = 4096: W4A4 814 -> 767 us, W4A16 861 -> 801).  Short K, more tiles
-    // or further splits measured slower: each split adds a partial-sum pass.
+    // at M = 4096: 384 tiles of 256 x 256, one per CU, so 1.5 rounds; 128 x
+    // 128 grids of that size, three workgroups per CU); split 2 evens the
+    // load (M = 4096: W4A4 814 -> 767 us, W4A16 861 -> 801; a 384-tile
+    // 128 x 128 grid at M = 1024: 246.6 -> 234.2 us).  Short K, more tiles or
+    // further splits measured slower: each split adds a partial-sum pass.
     if ((p.tile == A16Tile::k128x128_w64x64 || p.tile == A16Tile::k256x256_w128x64) && p.ksplit == 1 &&
         tiles >= 256 && tiles < 512 && ksteps >= 128)
         p.ksplit = 2;
