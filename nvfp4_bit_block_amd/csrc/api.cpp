@@ -136,10 +136,33 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
         return p;
     const bool short_k = K <= 4096;
     const bool lds = am == SAct::kPacked && M > 16;
-    if (short_k ? M < 3 : (am == SAct::kBf16 || am == SAct::kQuant || M < 5 || (M > 16 && !lds))) return p;
-    p.am = lds ? SAct::kPackedLds : am;
+    // bf16 activation on long rows, 5-16 batch rows: streamed through LDS
+    // (measured on MI355X, o_proj 6144 x 16384: 22.9-23.3 us against 23.4
+    // (GEMV, M = 5), 26.8 (tile, M = 8) and 27.1 us (tile, M = 16); with
+    // 32 or 64 rows its 512-K stages lose to the tiles, 37 / 49 against 28 /
+    // 37 us)
+    const bool lds_b = am == SAct::kBf16 && !short_k && M >= 5 && M <= 16;
+    if (short_k ? M < 3
+                : (am == SAct::kQuant || M < 5 || (am == SAct::kBf16 && !lds_b) || (am != SAct::kBf16 && M > 16 && !lds)))
+        return p;
+    p.am = lds ? SAct::kPackedLds : lds_b ? SAct::kBf16Lds : am;
     p.mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     auto krange_of = [&](int s) { return ((K / 128 + s - 1) / s) * 128; };
+    if (lds_b) {
+        // the fewest K splits first (each adds a partial-sum pass), then the
+        // wider weight tile: o_proj takes 32-row tiles unsplit (23.2 us at
+        // M = 8, against 24.6 us for 64-row tiles split in two)
+        for (int s = 1; s <= 8 && K / 128 >= s; s *= 2)
+            for (int nb = 4; nb >= 2; nb -= 2) {
+                if (((N + 16 * nb - 1) / (16 * nb)) * s < 192) continue;
+                p.use = true;
+                p.nb = nb;
+                p.ksplit = s;
+                p.krange = krange_of(s);
+                return p;
+            }
+        return p;
+    }
     if (M > 64) {
         // 65-128 rows (512-K stages): only on short rows with 64-row weight
         // tiles and no K split (measured on MI355X: q_b_proj M = 96 / 128
@@ -510,8 +533,8 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
         return fail(NVFP4_ERR_NULL_ARG, "gemv: all pointers are required%s");
     if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned4(w_global) || !aligned16(y))
         return fail(NVFP4_ERR_ALIGN, "gemv: pointers must be 16-byte aligned%s");
-    // short rows from M = 3: the stream kernel (when it needs no K split, so
-    // no workspace)
+    // the stream kernel when it needs no K split (so no workspace): short
+    // rows from M = 3, long rows from M = 5 (the activation through LDS)
     const StreamPlan sp = plan_stream(M, N, K, SAct::kBf16);
     if (sp.use && sp.ksplit == 1)
         return hip_status(run_stream(sp, x, nullptr, nullptr, M, N, K, w_codes, w_scales, w_global, y,

@@ -95,32 +95,36 @@ __device__ __forceinline__ void wait_stages(int n) {
 // 128 and, when WK < 8, the batch blocks into 8 / WK groups.
 template <int NB, int MB, SAct AM, int NS, int NCH, int CK = kChunkK>
 __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
-    using Op = typename std::conditional<AM == SAct::kBf16, bf16x8, f16x8>::type;
+    using Op = typename std::conditional<AM == SAct::kBf16 || AM == SAct::kBf16Lds, bf16x8, f16x8>::type;
     constexpr bool kPk = AM == SAct::kPacked || AM == SAct::kQuant;   // activation kept packed in registers
-    constexpr bool kLds = AM == SAct::kPackedLds;                     // packed activation streamed through LDS
+    constexpr bool kLdsP = AM == SAct::kPackedLds;                    // packed activation streamed through LDS
+    constexpr bool kLdsB = AM == SAct::kBf16Lds;                      // bf16 activation streamed through LDS
+    constexpr bool kLds = kLdsP || kLdsB;
     static_assert(CK == kChunkK || (kLds && CK == 512), "512-K stages stream the activation");
     constexpr int WK = CK / 128, WM = kWaves / WK, MBW = MB / WM;
     constexpr int RC = CK / 2, RSB = CK / 16;                 // code and scale bytes of a row per stage
     constexpr int NSLOT = RC / 16, NDW = RSB / 4;             // its 16-byte code slots and scale dwords
     constexpr int BN = 16 * NB, MP = kLds ? 16 * MB : 0;
+    constexpr int RA = 2 * CK, LPR = RA / 1024;               // bf16 activation: bytes of a row per stage, loads per row
     constexpr int CODE_BYTES = BN * RC, WBYTES = BN * (RC + RSB);
     constexpr int ACODE = WBYTES, ASCALE = WBYTES + MP * RC;          // activation rows of a stage (kLds)
     // a load instruction of a wave covers 1 KB of codes (1024 / RC rows) or
     // 256 bytes of scales (256 / RSB rows); every wave issues the same number
     // of each kind, and one numbered past the last slab loads zeros into a
     // 1 KB pad at the end of the stage
-    constexpr int NLC = BN * RC / 1024, NLS = BN * RSB / 256, NLCA = MP * RC / 1024, NLSA = MP * RSB / 256;
+    constexpr int NLC = BN * RC / 1024, NLS = BN * RSB / 256;
+    constexpr int NLCA = kLdsB ? MP * LPR : MP * RC / 1024, NLSA = kLdsB ? 0 : MP * RSB / 256;
     constexpr int LC = (NLC + kWaves - 1) / kWaves, LS = (NLS + kWaves - 1) / kWaves;
     constexpr int LCA = (NLCA + kWaves - 1) / kWaves, LSA = (NLSA + kWaves - 1) / kWaves;
     constexpr bool kPad = LC * kWaves != NLC || LS * kWaves != NLS || LCA * kWaves != NLCA || LSA * kWaves != NLSA;
-    constexpr int PAD = WBYTES + MP * (RC + RSB);
+    constexpr int PAD = WBYTES + MP * (kLdsB ? RA : RC + RSB);
     constexpr int STAGE = PAD + (kPad ? 1024 : 0);
     constexpr int L = LC + LS + LCA + LSA;                    // DMA loads per wave per stage
     constexpr int ROWS = 16 * MB, RSTR = BN + 4;             // reduction buffer [K unit][row][RSTR] fp32
     constexpr int RED_BYTES = WK * ROWS * RSTR * 4;
     constexpr int LDS = NS * STAGE > RED_BYTES ? NS * STAGE : RED_BYTES;
     static_assert(NB == 2 || NB == 4, "weight row blocks");
-    static_assert(!kLds || MB >= 2, "activation row blocks");
+    static_assert(!kLdsP || MB >= 2, "activation row blocks");
     static_assert(MB % WM == 0, "batch blocks per wave group");
     static_assert(NS >= 2 && NS <= 5 && LDS <= 160 * 1024, "LDS");
     static_assert(L * (NS - 2) <= 63, "vmcnt");
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const uint32_t KB = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);
     const u32x4 rb_c = make_rsrc(g.b_codes, (uint64_t)N * KB);
     const u32x4 rb_s = make_rsrc(g.b_scales, (uint64_t)N * KS);
-    const u32x4 ra_c = make_rsrc(kLds ? g.a : nullptr, kLds ? (uint64_t)M * KB : 0);
+    const u32x4 ra_c = make_rsrc(kLds ? g.a : nullptr, kLdsB ? (uint64_t)M * K * 2 : kLds ? (uint64_t)M * KB : 0);
     const u32x4 ra_s = make_rsrc(kLds ? g.a_scales : nullptr, kLds ? (uint64_t)M * KS : 0);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
 
@@ -178,12 +182,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
         for (int u = 0; u < LC; ++u) code_load(rb_c, w * LC + u, NLC, n0, N, kc, base, pad);
 #pragma unroll
         for (int u = 0; u < LS; ++u) scale_load(rb_s, w * LS + u, NLS, n0, N, kc, base + (uint32_t)CODE_BYTES, pad);
-        if constexpr (kLds) {
+        if constexpr (kLdsP) {
             // the chunk's activation rows, laid out like the weight rows
 #pragma unroll
             for (int u = 0; u < LCA; ++u) code_load(ra_c, w * LCA + u, NLCA, 0, M, kc, base + (uint32_t)ACODE, pad);
 #pragma unroll
             for (int u = 0; u < LSA; ++u) scale_load(ra_s, w * LSA + u, NLSA, 0, M, kc, base + (uint32_t)ASCALE, pad);
+        }
+        if constexpr (kLdsB) {
+            // bf16 activation rows, RA bytes each: load q fills 1 KB of row
+            // q / LPR, slot p (16 bytes, 8 values) <- the row's slot p ^ (row % 16),
+            // which spreads the fragment reads of 16 consecutive rows over
+            // the banks (the swizzle stays inside a 128-K unit of 16 slots)
+#pragma unroll
+            for (int u = 0; u < LCA; ++u) {
+                const int q = w * LCA + u, r = q / LPR;
+                const int slot = 64 * (q % LPR) + lane;
+                const int64_t kk = kc + 8 * (slot ^ (r & 15));
+                const bool in = q < NLCA && r < M && kk < k1;
+                lds_load16(ra_c, in ? (uint32_t)(r * K + kk) * 2u : kOob, 0u,
+                           q < NLCA ? base + (uint32_t)(ACODE + q * 1024) : pad);
+            }
         }
     };
     if constexpr (AM != SAct::kQuant) {
@@ -292,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
         }
-        if constexpr (kLds) {
+        if constexpr (kLdsP) {
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
                 const int b = wm * MBW + mb;
@@ -307,7 +326,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
                 if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
-                else if constexpr (kLds) bx[mb] = fp4x8_scaled_f16(word4(xl[mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
+                else if constexpr (kLdsP) bx[mb] = fp4x8_scaled_f16(word4(xl[mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
+                else if constexpr (kLdsB)
+                    bx[mb] = *reinterpret_cast<const Op*>(
+                        sb + ACODE + (16 * (wm * MBW + mb) + i16) * RA + 16 * ((16 * wk + 4 * grp + kk) ^ i16));
                 else bx[mb] = __builtin_bit_cast(Op, xa[c][mb][kk]);
             }
 #pragma unroll
@@ -388,30 +410,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 
 constexpr int kActBudget = 128;   // activation VGPRs per wave
 constexpr int act_regs(SAct am, int mb) {
-    return am == SAct::kPackedLds ? 0 : (am == SAct::kPacked ? 5 : 16) * mb;
+    return am == SAct::kPackedLds || am == SAct::kBf16Lds ? 0 : (am == SAct::kPacked ? 5 : 16) * mb;
 }
 
-// Bytes of one ring stage of the LDS-streamed form (weight and activation
+// Bytes of one ring stage of the LDS-streamed forms (weight and activation
 // rows, and the 1 KB pad when the loads do not divide evenly among the waves).
-template <int NB, int MB, int CK>
+template <int NB, int MB, int CK, bool BF16>
 constexpr int lds_stage_bytes() {
     constexpr int RC = CK / 2, RSB = CK / 16, BN = 16 * NB, MP = 16 * MB;
-    constexpr bool pad = (BN * RC / 1024) % kWaves || (BN * RSB / 256) % kWaves || (MP * RC / 1024) % kWaves ||
-                         (MP * RSB / 256) % kWaves;
-    return (BN + MP) * (RC + RSB) + (pad ? 1024 : 0);
+    constexpr int nla = BF16 ? MP * CK * 2 / 1024 : MP * RC / 1024, nlsa = BF16 ? 0 : MP * RSB / 256;
+    constexpr bool pad = (BN * RC / 1024) % kWaves || (BN * RSB / 256) % kWaves || nla % kWaves || nlsa % kWaves;
+    return BN * (RC + RSB) + (BF16 ? MP * CK * 2 : MP * (RC + RSB)) + (pad ? 1024 : 0);
 }
 
 template <int NB, int MB, SAct AM, int NCH>
 hipError_t launch_one(const StreamArgs& g, hipStream_t stream) {
-    if constexpr (NCH * act_regs(AM, MB) > kActBudget || (AM == SAct::kPackedLds && MB < 2)) {
+    constexpr bool kLds = AM == SAct::kPackedLds || AM == SAct::kBf16Lds;
+    // LDS-streamed forms: 512-K stages above 64 packed or 16 bf16 batch rows,
+    // and as many stages (up to four) as LDS holds
+    constexpr int CK = (AM == SAct::kPackedLds && MB > 4) || (AM == SAct::kBf16Lds && MB > 1) ? 512 : kChunkK;
+    constexpr int kLdsStage = lds_stage_bytes<NB, MB, CK, AM == SAct::kBf16Lds>();
+    if constexpr (NCH * act_regs(AM, MB) > kActBudget || (AM == SAct::kPackedLds && MB < 2) ||
+                  (kLds && 2 * kLdsStage > 160 * 1024)) {
         return hipErrorInvalidValue;
     } else {
-        // kPackedLds: 512-K stages above 64 batch rows, and as many stages
-        // (up to four) as LDS holds
-        constexpr int CK = AM == SAct::kPackedLds && MB > 4 ? 512 : kChunkK;
-        constexpr int kLdsStage = lds_stage_bytes<NB, MB, CK>();
-        constexpr int NS = AM == SAct::kPackedLds ? (4 * kLdsStage <= 160 * 1024 ? 4 : 3 * kLdsStage <= 160 * 1024 ? 3 : 2)
-                                                  : NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
+        constexpr int NS = kLds ? (4 * kLdsStage <= 160 * 1024 ? 4 : 3 * kLdsStage <= 160 * 1024 ? 3 : 2)
+                                : NCH == 1 ? 2 : NCH == 2 ? 3 : 4;
         const int64_t ntn = (g.N + 16 * NB - 1) / (16 * NB);
         hipLaunchKernelGGL((k_gemm_stream<NB, MB, AM, NS, NCH, CK>), dim3((unsigned)(ntn * g.ksplit)),
                            dim3(kThreads), 0, stream, g);
@@ -455,7 +479,7 @@ hipError_t launch_am(const StreamArgs& g, int nb, int mb, int nch, hipStream_t s
 // block and chunk for 16-bit values, 5 for packed codes (the in-register
 // quantization stages 16 per block and chunk until it has encoded them).
 int stream_max_chunks(SAct am, int mb) {
-    if (am == SAct::kPackedLds) return 1 << 20;   // no activation registers: any chunk count
+    if (am == SAct::kPackedLds || am == SAct::kBf16Lds) return 1 << 20;   // no activation registers: any chunk count
     int nch = 1;
     while (nch * 2 <= 16 && nch * 2 * act_regs(am, mb) <= kActBudget) nch *= 2;
     return nch;
@@ -475,6 +499,15 @@ hipError_t launch_gemm_stream(const StreamArgs& g, SAct am, int nb, int mb, hipS
         if (nb == 2) return mb == 2 ? launch_one<2, 2, SAct::kPackedLds, 1>(g, stream)
                           : mb == 4 ? launch_one<2, 4, SAct::kPackedLds, 1>(g, stream)
                           : mb == 8 ? launch_one<2, 8, SAct::kPackedLds, 1>(g, stream) : hipErrorInvalidValue;
+        return hipErrorInvalidValue;
+    }
+    if (am == SAct::kBf16Lds) {
+        if (nb == 4) return mb == 1 ? launch_one<4, 1, SAct::kBf16Lds, 1>(g, stream)
+                          : mb == 2 ? launch_one<4, 2, SAct::kBf16Lds, 1>(g, stream)
+                          : mb == 4 ? launch_one<4, 4, SAct::kBf16Lds, 1>(g, stream) : hipErrorInvalidValue;
+        if (nb == 2) return mb == 1 ? launch_one<2, 1, SAct::kBf16Lds, 1>(g, stream)
+                          : mb == 2 ? launch_one<2, 2, SAct::kBf16Lds, 1>(g, stream)
+                          : mb == 4 ? launch_one<2, 4, SAct::kBf16Lds, 1>(g, stream) : hipErrorInvalidValue;
         return hipErrorInvalidValue;
     }
     switch (am) {

@@ -198,6 +198,7 @@ enum class SAct : int {
     kPacked = 2,  // NVFP4 codes [M, K/2] + E4M3 scale bytes [M, K/16]
     kQuant = 3,   // bf16 [M, K], quantized in registers under *a_global (static)
     kPackedLds = 4,  // as kPacked, streamed through LDS with the weights (M > 16)
+    kBf16Lds = 5,    // as kBf16, streamed through LDS with the weights (long rows)
 };
 
 struct StreamArgs {
@@ -215,7 +216,8 @@ struct StreamArgs {
 
 // Y = A W^T for 1 <= M <= 16 mb on a grid of ceil(N / (16 nb)) x ksplit
 // workgroups of 8 waves, nb in {2, 4}, mb in {1, 2, 4} (kPackedLds: 2, 4
-// or 8, the last on 512-K ring stages); K % 128 == 0 and
+// or 8, the last on 512-K ring stages; kBf16Lds: 1, 2 or 4, the last two on
+// 512-K ring stages); K % 128 == 0 and
 // N * K / 2 < 2^31.  Each K range may hold at most stream_max_chunks(am, mb)
 // chunks of 1024 (rounded up to a power of two); hipErrorInvalidValue
 // otherwise.

@@ -1,5 +1,6 @@
 """GPU parity of the weight-streaming small-batch GEMM (the planner sends
 W4A4, pre-packed W4A4 and W4A16 products with M <= 64 to it on short rows,
+W4A16 with M = 5..16 on long rows (bf16 activation streamed through LDS),
 pre-packed/one-call W4A4 with M = 65..128 on short rows (512-K ring stages,
 the waves split into four K units and two batch halves), and
 pre-packed/one-call W4A4 with M = 5..64 on long rows) against the
@@ -56,7 +57,8 @@ def test_stream_w4a4_and_packed(orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 12288, 2048), (17, 12288, 1152), (50, 12290, 640), (64, 12288, 4096),
-                                   (8, 16384, 2048)])
+                                   (8, 16384, 2048), (5, 6144, 16384), (8, 6144, 16384), (16, 6160, 8192),
+                                   (12, 3072, 32768)])
 def test_stream_w4a16(orc, M, N, K):
     print(f"stream w4a16 M={M} N={N} K={K}", flush=True)
     w = wl.layer_weight((N, K), seed=M + 5 + N % 89)
