@@ -70,10 +70,18 @@ __device__ __forceinline__ uint32_t word4(const uint4& v, int k) {
 }
 
 // Eight weight codes -> eight MFMA operand values q * s (exact).
-__device__ __forceinline__ f16x8 decode8(uint32_t w, float s, f16x8*) { return fp4x8_scaled_f16(w, (_Float16)s); }
+__device__ __forceinline__ f16x8 decode8(uint32_t w, _Float16 s, f16x8*) { return fp4x8_scaled_f16(w, s); }
 __device__ __forceinline__ bf16x8 decode8(uint32_t w, float s, bf16x8*) {
     return __builtin_bit_cast(bf16x8, fp4x8_scaled_bf16_bits(w, s));
 }
+// Two E4M3 scale bytes (bits 0-7, 8-15) -> the pair in the decode's
+// precision, through the exact FP8 -> fp32 conversion (every E4M3 value is
+// an f16 value, so the narrowing is exact too).
+__device__ __forceinline__ f16x2 scale_pair(uint32_t w, f16x8*) {
+    const f32x2 f = e4m3x2_to_f32(w);
+    return f16x2{(_Float16)f.x, (_Float16)f.y};
+}
+__device__ __forceinline__ f32x2 scale_pair(uint32_t w, bf16x8*) { return e4m3x2_to_f32(w); }
 
 // Wait until at most n vector memory operations of this wave are in flight
 // (n a multiple of the per-stage load count, at most NS - 2 stages).
@@ -150,58 +158,88 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
 
     // ---- 1. the first NS - 1 chunks of weights into the ring
-    // chunk c into stage st: code load q = w LC + u covers rows
-    // (1024 / RC) q + lane / NSLOT, slot lane % NSLOT <- the row's 16-byte
-    // chunk (lane % NSLOT) ^ (row % 8); scale load q covers rows
-    // (256 / RSB) q + lane / NDW, dword slot lane % NDW <- dword
-    // (lane % NDW) ^ (row % NDW).  Pieces past N, M or the K range read zeros.
+    // Code load q = w LC + u covers rows (1024 / RC) q + lane / NSLOT, slot
+    // lane % NSLOT <- the row's 16-byte chunk (lane % NSLOT) ^ (row % 8);
+    // scale load q covers rows (256 / RSB) q + lane / NDW, dword slot
+    // lane % NDW <- dword (lane % NDW) ^ (row % NDW).  The per-lane offsets of
+    // the range's first chunk are computed once (an offset past every buffer
+    // for pieces past N or M, which read zeros); a chunk adds its K offset.
+    // Pieces past the K range are loaded but never multiplied: k1 is a
+    // multiple of 128 and a wave skips any 128-K unit at or past it; past the
+    // end of the last row they read zeros.
+    // Workgroups start at different chunks of their range (chunk c of the
+    // loop is chunk (c + rot) mod nchunks), so that the chip's concurrent
+    // reads spread over the rows instead of all meeting at one K offset.
+    const int rot = (int)(blockIdx.x % (unsigned)nchunks);
+    auto rchunk = [&](int c) { return c + rot < nchunks ? c + rot : c + rot - nchunks; };   // c < nchunks
     constexpr int RPC = 1024 / RC, RPS = 256 / RSB;
-    // (q and nq are wave-uniform, so is the LDS destination)
-    auto code_load = [&](const u32x4& rs, int q, int nq, int64_t row0, int64_t rows, int64_t kc, uint32_t region,
-                         uint32_t pad) {
+    constexpr int NOCA = kLds ? LCA : 1, NOSA = kLdsP ? LSA : 1;
+    uint32_t oc[LC], os[LS], oca[NOCA], osa[NOSA];
+    auto code_off = [&](int q, int nq, int64_t row0, int64_t rows) -> uint32_t {
         const int r = RPC * q + lane / NSLOT;
         const int unit = (lane % NSLOT) ^ (r & 7);
-        const int64_t row = row0 + r, kk = kc + 32 * unit;
-        const bool in = q < nq && row < rows && kk < k1;
-        lds_load16(rs, in ? (uint32_t)row * KB + (uint32_t)(kk / 2) : kOob, 0u,
-                   q < nq ? region + (uint32_t)(q * 1024) : pad);
+        const int64_t row = row0 + r;
+        return q < nq && row < rows ? (uint32_t)row * KB + (uint32_t)((k0 + 32 * unit) / 2) : kOob;
     };
-    auto scale_load = [&](const u32x4& rs, int q, int nq, int64_t row0, int64_t rows, int64_t kc, uint32_t region,
-                          uint32_t pad) {
+    auto scale_off = [&](int q, int nq, int64_t row0, int64_t rows) -> uint32_t {
         const int r = RPS * q + lane / NDW;
         const int d = (lane % NDW) ^ (r & (NDW - 1));
-        const int64_t row = row0 + r, kk = kc + 64 * d;
-        const bool in = q < nq && row < rows && kk < k1;
-        lds_load4(rs, in ? (uint32_t)row * KS + (uint32_t)(kk / 16) : kOob, 0u,
-                  q < nq ? region + (uint32_t)(q * 256) : pad);
+        const int64_t row = row0 + r;
+        return q < nq && row < rows ? (uint32_t)row * KS + (uint32_t)((k0 + 64 * d) / 16) : kOob;
     };
+#pragma unroll
+    for (int u = 0; u < LC; ++u) oc[u] = code_off(w * LC + u, NLC, n0, N);
+#pragma unroll
+    for (int u = 0; u < LS; ++u) os[u] = scale_off(w * LS + u, NLS, n0, N);
+    if constexpr (kLdsP) {
+#pragma unroll
+        for (int u = 0; u < LCA; ++u) oca[u] = code_off(w * LCA + u, NLCA, 0, M);
+#pragma unroll
+        for (int u = 0; u < LSA; ++u) osa[u] = scale_off(w * LSA + u, NLSA, 0, M);
+    }
+    if constexpr (kLdsB) {
+        // bf16 activation rows, RA bytes each: load q fills 1 KB of row
+        // q / LPR, slot p (16 bytes, 8 values) <- the row's slot p ^ (row % 16),
+        // which spreads the fragment reads of 16 consecutive rows over the
+        // banks (the swizzle stays inside a 128-K unit of 16 slots)
+#pragma unroll
+        for (int u = 0; u < LCA; ++u) {
+            const int q = w * LCA + u, r = q / LPR;
+            const int slot = 64 * (q % LPR) + lane;
+            oca[u] = q < NLCA && r < M ? (uint32_t)((r * K + k0 + 8 * (slot ^ (r & 15))) * 2) : kOob;
+        }
+    }
     auto issue = [&](int c, int st) {
         const uint32_t base = lds0 + (uint32_t)(st * STAGE), pad = base + (uint32_t)PAD;
-        const int64_t kc = k0 + (int64_t)c * CK;
+        const uint32_t dk = (uint32_t)(rchunk(c) * CK);   // K offset of the chunk in the range
 #pragma unroll
-        for (int u = 0; u < LC; ++u) code_load(rb_c, w * LC + u, NLC, n0, N, kc, base, pad);
+        for (int u = 0; u < LC; ++u) {
+            const int q = w * LC + u;
+            lds_load16(rb_c, oc[u] + dk / 2, 0u, q < NLC ? base + (uint32_t)(q * 1024) : pad);
+        }
 #pragma unroll
-        for (int u = 0; u < LS; ++u) scale_load(rb_s, w * LS + u, NLS, n0, N, kc, base + (uint32_t)CODE_BYTES, pad);
+        for (int u = 0; u < LS; ++u) {
+            const int q = w * LS + u;
+            lds_load4(rb_s, os[u] + dk / 16, 0u, q < NLS ? base + (uint32_t)(CODE_BYTES + q * 256) : pad);
+        }
         if constexpr (kLdsP) {
             // the chunk's activation rows, laid out like the weight rows
 #pragma unroll
-            for (int u = 0; u < LCA; ++u) code_load(ra_c, w * LCA + u, NLCA, 0, M, kc, base + (uint32_t)ACODE, pad);
+            for (int u = 0; u < LCA; ++u) {
+                const int q = w * LCA + u;
+                lds_load16(ra_c, oca[u] + dk / 2, 0u, q < NLCA ? base + (uint32_t)(ACODE + q * 1024) : pad);
+            }
 #pragma unroll
-            for (int u = 0; u < LSA; ++u) scale_load(ra_s, w * LSA + u, NLSA, 0, M, kc, base + (uint32_t)ASCALE, pad);
+            for (int u = 0; u < LSA; ++u) {
+                const int q = w * LSA + u;
+                lds_load4(ra_s, osa[u] + dk / 16, 0u, q < NLSA ? base + (uint32_t)(ASCALE + q * 256) : pad);
+            }
         }
         if constexpr (kLdsB) {
-            // bf16 activation rows, RA bytes each: load q fills 1 KB of row
-            // q / LPR, slot p (16 bytes, 8 values) <- the row's slot p ^ (row % 16),
-            // which spreads the fragment reads of 16 consecutive rows over
-            // the banks (the swizzle stays inside a 128-K unit of 16 slots)
 #pragma unroll
             for (int u = 0; u < LCA; ++u) {
-                const int q = w * LCA + u, r = q / LPR;
-                const int slot = 64 * (q % LPR) + lane;
-                const int64_t kk = kc + 8 * (slot ^ (r & 15));
-                const bool in = q < NLCA && r < M && kk < k1;
-                lds_load16(ra_c, in ? (uint32_t)(r * K + kk) * 2u : kOob, 0u,
-                           q < NLCA ? base + (uint32_t)(ACODE + q * 1024) : pad);
+                const int q = w * LCA + u;
+                lds_load16(ra_c, oca[u] + 2 * dk, 0u, q < NLCA ? base + (uint32_t)(ACODE + q * 1024) : pad);
             }
         }
     };
@@ -230,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
         const_cast<uint8_t*>(g.a_scales), (short)0, (int)(AM == SAct::kPacked ? M * K / 16 : 0), (int)kRsrcWord3);
 #pragma unroll
     for (int c = 0; c < (kLds ? 0 : NCH); ++c) {
-        const int64_t ku = k0 + (int64_t)c * kChunkK + 128 * w;     // the wave's unit (uniform)
+        const int64_t ku = k0 + (int64_t)rchunk(c) * kChunkK + 128 * w;   // the wave's unit (uniform)
         const bool kin = c < nchunks && ku < k1;
         const int64_t ka = ku + 32 * grp;
 #pragma unroll
@@ -296,28 +334,54 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
 
     // (the wave's batch blocks are wm MBW .. wm MBW + MBW - 1; with the
     // activation in registers WM = 1 and they are all MB)
-    auto compute = [&](int c, int st) {
+    // the wave's fragments of one chunk, read from its ring stage
+    using Sc = typename std::conditional<std::is_same<Op, f16x8>::value, f16x2, f32x2>::type;
+    constexpr int FP = kLdsP ? MBW : 1, FB = kLdsB ? MBW : 1;
+    // (scale bytes stay raw here: converting them would make the wave wait
+    // for its LDS reads before it issues the next chunk's loads)
+    struct Frag {
+        uint4 cw[NB];       // weight codes
+        uint32_t sw[NB];    // their two block scales
+        uint4 xl[FP];       // packed activation codes (kPackedLds)
+        uint32_t xsc[FP];   // and scales
+        uint4 xb[FB][4];    // bf16 activation operands (kBf16Lds)
+    };
+    auto fetch = [&](int st) {
         const uint8_t* sb = smem + st * STAGE;
-        uint4 cw[NB];
-        f32x2 sw[NB];
+        Frag f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            cw[nb] = *reinterpret_cast<const uint4*>(sb + fcode + nb * 16 * RC);
-            sw[nb] = e4m3x2_to_f32(*reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * RSB));
-        }
-        f32x2 xsc[MBW];
-        uint4 xl[kLds ? MBW : 1];
-        if constexpr (kPk) {
-#pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) xsc[mb] = e4m3x2_to_f32(xs[c][mb]);
+            f.cw[nb] = *reinterpret_cast<const uint4*>(sb + fcode + nb * 16 * RC);
+            f.sw[nb] = *reinterpret_cast<const uint16_t*>(sb + fscale + nb * 16 * RSB);
         }
         if constexpr (kLdsP) {
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
                 const int b = wm * MBW + mb;
-                xl[mb] = *reinterpret_cast<const uint4*>(sb + ACODE + fcode + b * 16 * RC);
-                xsc[mb] = e4m3x2_to_f32(
-                    *reinterpret_cast<const uint16_t*>(sb + ASCALE + (fscale - CODE_BYTES) + b * 16 * RSB));
+                f.xl[mb] = *reinterpret_cast<const uint4*>(sb + ACODE + fcode + b * 16 * RC);
+                f.xsc[mb] = *reinterpret_cast<const uint16_t*>(sb + ASCALE + (fscale - CODE_BYTES) + b * 16 * RSB);
+            }
+        }
+        if constexpr (kLdsB) {
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    f.xb[mb][kk] = *reinterpret_cast<const uint4*>(
+                        sb + ACODE + (16 * (wm * MBW + mb) + i16) * RA + 16 * ((16 * wk + 4 * grp + kk) ^ i16));
+        }
+        return f;
+    };
+    auto multiply = [&](int c, const Frag& f) {
+        f16x2 xsc[(kPk || kLdsP) ? MBW : 1];
+        Sc sw[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sw[nb] = scale_pair(f.sw[nb], (Op*)nullptr);
+        if constexpr (kPk || kLdsP) {
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb) {
+                if constexpr (kPk) xsc[mb] = scale_pair(xs[c][mb], (f16x8*)nullptr);
+                else xsc[mb] = scale_pair(f.xsc[mb], (f16x8*)nullptr);
             }
         }
 #pragma unroll
@@ -325,27 +389,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm_stream(StreamArgs g) {
             Op bx[MBW];
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb) {
-                if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
-                else if constexpr (kLdsP) bx[mb] = fp4x8_scaled_f16(word4(xl[mb], kk), (_Float16)(kk < 2 ? xsc[mb].x : xsc[mb].y));
-                else if constexpr (kLdsB)
-                    bx[mb] = *reinterpret_cast<const Op*>(
-                        sb + ACODE + (16 * (wm * MBW + mb) + i16) * RA + 16 * ((16 * wk + 4 * grp + kk) ^ i16));
+                if constexpr (kPk) bx[mb] = fp4x8_scaled_f16(word4(xc[c][mb], kk), kk < 2 ? xsc[mb].x : xsc[mb].y);
+                else if constexpr (kLdsP)
+                    bx[mb] = fp4x8_scaled_f16(word4(f.xl[mb], kk), kk < 2 ? xsc[mb].x : xsc[mb].y);
+                else if constexpr (kLdsB) bx[mb] = __builtin_bit_cast(Op, f.xb[mb][kk]);
                 else bx[mb] = __builtin_bit_cast(Op, xa[c][mb][kk]);
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const Op av = decode8(word4(cw[nb], kk), kk < 2 ? sw[nb].x : sw[nb].y, (Op*)nullptr);
+                const Op av = decode8(word4(f.cw[nb], kk), kk < 2 ? sw[nb].x : sw[nb].y, (Op*)nullptr);
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb) acc[nb][mb] = mfma16(av, bx[mb], acc[nb][mb]);
             }
         }
     };
 
-    // refill the stage multiplied in iteration c - 1 (all waves passed the
-    // barrier after it), multiply chunk c, wait for chunk c + 1
+    // read chunk c's fragments, refill the stage multiplied in iteration
+    // c - 1 (all waves passed the barrier after it) while they arrive,
+    // multiply chunk c, wait for chunk c + 1
     auto iteration = [&](int c, int cr) {
+        const bool mine = k0 + (int64_t)rchunk(c) * CK + 128 * wk < k1;
+        Frag f;
+        if (mine) f = fetch(c % NS);
         if (c + NS - 1 < nchunks) issue(c + NS - 1, (c + NS - 1) % NS);
-        if (k0 + (int64_t)c * CK + 128 * wk < k1) compute(cr, c % NS);
+        if (mine) multiply(cr, f);
         if (c + 1 < nchunks) {
             wait_stages<L>(min(NS - 2, nchunks - 2 - c));
             __syncthreads();

@@ -27,17 +27,22 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t bytes) {
     return r;
 }
 // Global -> LDS loads: lane l of the wave writes its 16 (or 4) bytes at LDS
-// byte address lds + 16 l (4 l); lds is wave-uniform and travels in M0 (one
-// wait state after the M0 write is required before the load).  Written as
-// asm so that the compiler does not make every later LDS read wait for them:
-// the K loop waits for them itself (vmcnt) before its barrier.  They have no
-// register results.
+// byte address lds + 16 l (4 l); lds is wave-uniform and travels in M0.
+// Written as asm so that the compiler does not make every later LDS read
+// wait for them: the K loop waits for them itself (vmcnt) before its
+// barrier.  They have no register results.
+// The compiler's hazard checks do not see the load inside the asm, so the
+// asm supplies the wait states itself: one after the M0 write, and five
+// after a VALU write of an SGPR the load reads.  The second case arises
+// when the compiler restores a spilled resource word with v_readlane just
+// before the asm; without the wait the load can take a stale descriptor
+// word and read from a wrong address.
 __device__ __forceinline__ void lds_load16(u32x4 r, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_load4(u32x4 r, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
