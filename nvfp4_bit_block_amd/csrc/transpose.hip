@@ -27,12 +27,17 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------- columnwise quantize --
 // Tile: 128 rows x 64 columns of x.  Load: 16 bytes (8 columns) per thread,
-// 8 threads per row.  LDS holds the tile row-major with rows padded by one
-// word.  Encode: thread t owns the column pair (2 (t / 8), +1) and the
-// 16-row block t % 8; it reads 16 words (both columns of one row each),
-// regroups them into bf16 pairs along R, and encodes one block per column.
+// 8 threads per row.  LDS holds the tile row-major, 32 words (64 columns) per
+// row, with word w of row r stored at w ^ (8 ((r / 16) mod 4)): a wave's
+// encode reads (8 column pairs x 8 row blocks) then fall on 32 different
+// banks, and the 16-byte row pieces stay aligned for 16-byte stores.
+// Encode: thread t owns the column pair (2 (t / 8), +1) and the 16-row block
+// t % 8; it reads 16 words (both columns of one row each), regroups them
+// into bf16 pairs along R, and encodes one block per column.
 constexpr int kQR = 128, kQC = 64;
-constexpr int kQStride = kQC / 2 + 1;  // words per LDS row
+constexpr int kQWords = kQC / 2;    // words per LDS row
+
+__device__ __forceinline__ int qc_word(int r, int w) { return r * kQWords + (w ^ (((r >> 4) & 3) << 3)); }
 
 template <ScaleMode MODE>
 __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __restrict__ x, int64_t R,
@@ -41,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
                                                             uint8_t* __restrict__ codes_t,
                                                             uint8_t* __restrict__ scales_t,
                                                             float* __restrict__ global_out) {
-    __shared__ uint32_t tile[kQR * kQStride];
+    __shared__ __align__(16) uint32_t tile[kQR * kQWords];
     float Sg;
     if constexpr (MODE == ScaleMode::kDynamic) {
         uint32_t m = 0;
@@ -68,11 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
         const int64_t r = r0 + lr, c = c0 + lc;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (r < R && c < C) v = load_nt16(x + r * C + c);   // C % 8 == 0
-        uint32_t* dst = tile + lr * kQStride + lc / 2;
-        dst[0] = v.x;
-        dst[1] = v.y;
-        dst[2] = v.z;
-        dst[3] = v.w;
+        *reinterpret_cast<uint4*>(tile + qc_word(lr, lc / 2)) = v;
     }
     __syncthreads();
 
@@ -83,8 +84,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_cols(const uint16_t* __re
     uint32_t a[8], b[8];                   // bf16 pairs along R: column c, column c + 1
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t w0 = tile[(16 * blk + 2 * i) * kQStride + cp];
-        const uint32_t w1 = tile[(16 * blk + 2 * i + 1) * kQStride + cp];
+        const uint32_t w0 = tile[qc_word(16 * blk + 2 * i, cp)];
+        const uint32_t w1 = tile[qc_word(16 * blk + 2 * i + 1, cp)];
         a[i] = (w0 & 0xFFFFu) | (w1 << 16);
         b[i] = (w0 >> 16) | (w1 & 0xFFFF0000u);
     }
