@@ -14,15 +14,19 @@
 //     stream never waits for a second round of workgroups;
 //   * the weights move from HBM straight into LDS (buffer_load ... lds, each
 //     instruction 1 KB of two contiguous 512-byte row pieces, or 256 bytes of
-//     scales), in chunks of 1024 K through an NS-stage ring, NS - 1 chunks
-//     in flight;
-//   * the activation slice a wave needs for the whole K range is loaded into
-//     registers once, in the prologue (so the ring's vmcnt waits never wait
-//     on it): as 16-bit values (bf16 for W4A16, or the f16 products
-//     q * s of an already quantized activation), as packed NVFP4 codes and
-//     scale bytes decoded to exact f16 q * s at use, or as bf16 values that
-//     the wave quantizes in registers under the static input scale with the
-//     quantizer's block rule (then kept as packed codes);
+//     scales), in chunks of 1024 K (512 K when up to 128 activation rows
+//     share the stage) through an NS-stage ring, NS - 1 chunks in flight;
+//     workgroups start at different chunks of their K range so that the
+//     chip's concurrent reads spread over the rows;
+//   * the activation slice a wave needs for the whole K range is either
+//     loaded into registers once, in the prologue (so the ring's vmcnt waits
+//     never wait on it): as 16-bit values (bf16 for W4A16, or the f16
+//     products q * s of an already quantized activation), as packed NVFP4
+//     codes and scale bytes decoded to exact f16 q * s at use, or as bf16
+//     values that the wave quantizes in registers under the static input
+//     scale with the quantizer's block rule (then kept as packed codes); or,
+//     where it does not fit the registers (packed above 16 rows, bf16 on long
+//     rows), streamed through the same ring beside the weights;
 //   * K is split across the 8 waves (wave w takes K [128 w, 128 w + 128) of
 //     every chunk, so each activation element is loaded once per
 //     workgroup); a wave decodes its weight fragments from LDS to exact q * s
