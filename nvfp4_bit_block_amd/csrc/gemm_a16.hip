@@ -794,10 +794,21 @@ hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int
     const int64_t total = M * N;
     switch (ksplit) {
         case 2: return launch_reduce_ks<2>(partial, total, g0, g1, y, stream);
+        case 3: return launch_reduce_ks<3>(partial, total, g0, g1, y, stream);
         case 4: return launch_reduce_ks<4>(partial, total, g0, g1, y, stream);
+        case 5: return launch_reduce_ks<5>(partial, total, g0, g1, y, stream);
+        case 6: return launch_reduce_ks<6>(partial, total, g0, g1, y, stream);
+        case 7: return launch_reduce_ks<7>(partial, total, g0, g1, y, stream);
         case 8: return launch_reduce_ks<8>(partial, total, g0, g1, y, stream);
+        case 9: return launch_reduce_ks<9>(partial, total, g0, g1, y, stream);
+        case 10: return launch_reduce_ks<10>(partial, total, g0, g1, y, stream);
+        case 11: return launch_reduce_ks<11>(partial, total, g0, g1, y, stream);
+        case 12: return launch_reduce_ks<12>(partial, total, g0, g1, y, stream);
+        case 13: return launch_reduce_ks<13>(partial, total, g0, g1, y, stream);
+        case 14: return launch_reduce_ks<14>(partial, total, g0, g1, y, stream);
+        case 15: return launch_reduce_ks<15>(partial, total, g0, g1, y, stream);
         case 16: return launch_reduce_ks<16>(partial, total, g0, g1, y, stream);
-        default: return hipErrorInvalidValue;   // the split-K plan uses powers of two up to 16
+        default: return hipErrorInvalidValue;   // the split-K plans use 2 .. 16 splits
     }
 }
 

@@ -120,6 +120,28 @@ def test_gemm_shapes(orc, M, N, K):
     _gemm_case(orc, M, N, K, seed=M * 7 + N)
 
 
+# long rows above M = 128 take the 256 x 256 tile with K split 256 / tiles
+# ways: (300, 3072, 8192) 24 tiles, split 10 (the last split 11 of 128 K
+# steps); (300, 6144, 4352) 48 tiles, split 5 over 68 steps; (600, 3072,
+# 8192) 36 tiles, split 7; (600, 6144, 8192) 72 tiles, split 3
+@pytest.mark.parametrize("M,N,K", [(300, 3072, 8192), (300, 6144, 4352), (600, 3072, 8192), (600, 6144, 8192)])
+def test_gemm_long_row_splits(orc, M, N, K):
+    w = wl.layer_weight((N, K), seed=M + N % 89)
+    x = wl.activations(M, K, seed=M * 5 + K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    y16 = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    rng = np.random.default_rng(M + N)
+    rows = np.sort(np.concatenate([rng.choice(M, 40, replace=False), [0, M - 1]]))
+    rows = np.unique(rows)
+    cols = np.unique(np.sort(np.concatenate([rng.choice(N, 80, replace=False), [0, N - 1]])))
+    assert_close(y[np.ix_(rows, cols)], orc.gemm_w4a4(x[rows], isc, c0[cols], s0[cols], g0),
+                 f"gemm {M}x{N}x{K}")
+    assert_close(y16[np.ix_(rows, cols)], orc.gemv_w4a16(x[rows], c0[cols], s0[cols], g0),
+                 f"gemm w4a16 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
 @pytest.mark.parametrize("M", list(wl.GEMM_M_SWEEP))
 def test_gemm_layers_sampled(orc, name, M):
