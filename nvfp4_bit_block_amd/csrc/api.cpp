@@ -84,27 +84,26 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     const int64_t bm = a16_tile_rows(p.tile), bn = a16_tile_cols(p.tile);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t ksteps = K / 64;
-    // split K until about one workgroup per CU.  Up to M = 64 the split stops
-    // before the count exceeds 256: measured at M = 32 and 64 on o_proj
-    // (6144 x 16384), 192 workgroups (split 8) beat 384 (split 16) by 7-14 %,
-    // each further split adding a partial-sum pass over M x N and a workgroup
-    // prologue for the same weight stream.  The 256 x 256 tile on long rows
-    // runs one workgroup per CU (M = 256: split 8 69.9 us against split 4
-    // 100.1 us; M = 2048 unsplit 419 against split 2 445 us) and takes the
-    // split that comes closest to 256 of them.
+    // split K until about one workgroup per CU.  Up to M = 64, and for the
+    // 256 x 256 tile on long rows, the split stops at 256 workgroups and may
+    // take any count: measured at M = 32 and 64 on o_proj (6144 x 16384), 192
+    // workgroups (split 8) beat 384 (split 16) by 7-14 %, each further split
+    // adding a partial-sum pass over M x N and a workgroup prologue for the
+    // same weight stream; the 256 x 256 tile needs its one workgroup per CU
+    // (M = 256: split 8 69.9 us against split 4 100.1 us; M = 2048 unsplit
+    // 419 against split 2 445 us).
     const bool one_per_cu = long_wide && p.tile == A16Tile::k256x256_w128x64;
-    auto wants_split = [&]() {
-        return M <= 64 ? tiles * p.ksplit * 2 <= 256 : tiles * p.ksplit < 256;
-    };
-    if (one_per_cu) {
+    if (one_per_cu || M <= 64) {
         // as many workgroups as fit one per CU, with any split count: 256 / tiles
         // (measured on MI355X, o_proj 6144 x 16384, f16 / bf16 activation: M = 256
         // split 10 (240 workgroups) 68.3 / 72.3 us against split 8 71.1 / 75.8;
-        // M = 512 split 5 107.4 / 114.4 against split 4 118.8 / 125.2)
+        // M = 512 split 5 107.4 / 114.4 against split 4 118.8 / 125.2; M = 32 on
+        // 32 x 256 tiles split 10 22.9 / 26.4 against split 8 23.4 / 27.9; M = 64
+        // on 64 x 256 tiles 30.7 / 34.1 against 31.5 / 35.7)
         if (tiles < 256) p.ksplit = (int)std::min<int64_t>(16, 256 / tiles);
         while (p.ksplit > 1 && ksteps / p.ksplit < 8) --p.ksplit;
     } else {
-        while (wants_split() && p.ksplit < 16 && ksteps / (p.ksplit * 2) >= 8) p.ksplit *= 2;
+        while (tiles * p.ksplit < 256 && p.ksplit < 16 && ksteps / (p.ksplit * 2) >= 8) p.ksplit *= 2;
     }
     // 256-511 tiles on long K leave some CUs one tile and others two (o_proj
     // at M = 4096: 384 tiles of 256 x 256, one per CU, so 1.5 rounds; 128 x
