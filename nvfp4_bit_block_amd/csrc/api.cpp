@@ -33,10 +33,13 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // ----------------------------------------------------------- GEMM planning --
 
+int64_t gemm_chunk_rows(int64_t M, int64_t K);
+
 struct GemmPlan {
     bool gemv = false;   // M <= 8: decoded activation + GEMV
     A16Tile tile = A16Tile::k256x256_w128x64;
-    int ksplit = 1;
+    int ksplit = 1;   // K splits, or with stream-K the partial slots
+    int sk_wgs = 0;   // stream-K workgroups (0: none)
 };
 
 // Tile and split-K choice for the W4A4 GEMM (measured on MI355X: the
@@ -114,6 +117,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     if ((p.tile == A16Tile::k128x128_w64x64 || p.tile == A16Tile::k256x256_w128x64) && p.ksplit == 1 &&
         tiles >= 256 && tiles < 512 && ksteps >= 128)
         p.ksplit = 2;
+    // Stream-K where the one-per-CU split leaves many CUs idle: 256
+    // workgroups share the tiles' K steps evenly, each tile's parts summed in
+    // order afterwards.  The chip does not run 256 busy CUs much faster than
+    // 192, and the finish reads every part, so it pays only below about 70 %
+    // of the CUs (measured on MI355X, o_proj 6144 x 16384, f16 / bf16
+    // activation: M = 1536, 144 workgroups unsplit, 359.7 / 376.2 -> 306.6 /
+    // 319.0 us; M = 1024, 192 at split 2, 227.5 / 227.5 -> 222.2 / 223.8; M =
+    // 2048, 192 unsplit, 382.0 / 417.4 -> 387.2 / 407.0; M = 768, 216 at
+    // split 3, 156.7 / 166.8 -> 161.6 / 173.3).  One launch (the rows fit
+    // one buffer resource), at least 8 K steps per workgroup.
+    if (one_per_cu && tiles * p.ksplit <= 176 && gemm_chunk_rows(M, K) >= M && tiles * ksteps >= 256 * 8) {
+        const int slots = streamk_slots(M, N, K, p.tile, 256);
+        if (slots >= 2 && slots <= 8) {
+            p.sk_wgs = 256;
+            p.ksplit = slots;
+        }
+    }
     return p;
 }
 
@@ -313,7 +333,15 @@ hipError_t run_gemm_tiles(const GemmPlan& p, const uint16_t* a, AFmt afmt, const
         g.K = K;
         g.ksplit = p.ksplit;
         hipError_t e;
-        if (p.ksplit > 1) {
+        if (p.sk_wgs > 0) {
+            g.ksplit = 1;
+            g.sk_wgs = p.sk_wgs;
+            g.out = partial;
+            g.ldo = N;
+            e = launch_gemm_a16(g, afmt, Epi::kPartialF32, p.tile, 0, s);
+            if (e != hipSuccess) return e;
+            e = launch_streamk_reduce(partial, rows, N, K, p.tile, p.sk_wgs, w_global, a_global, y + r0 * N, s);
+        } else if (p.ksplit > 1) {
             g.out = partial;
             g.ldo = N;
             e = launch_gemm_a16(g, afmt, Epi::kPartialF32, p.tile, 0, s);

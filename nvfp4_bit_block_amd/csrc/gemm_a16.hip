@@ -36,6 +36,8 @@
 // chunks of a row are permuted so that the 16-byte fragment reads of 16
 // consecutive rows fall on distinct banks: A row r keeps its chunk c in slot
 // c ^ ((r / 2) % 8), B column n its code half h in slot h ^ ((n / 8) % 2).
+#include <algorithm>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_dma.hpp"
 #include "nvfp4_encode.hpp"
@@ -77,6 +79,12 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int kk) {
 
 constexpr int kGroupM = 8;   // m-tiles per band in the ungrouped tile order
 
+// Stream-K: workgroup w of W takes global K steps [floor(w S / W),
+// floor((w + 1) S / W)); the one whose range holds step x.
+__host__ __device__ __forceinline__ int sk_first(int64_t x, int W, int64_t S) {
+    return (int)(((x + 1) * (int64_t)W - 1) / S);
+}
+
 // Tile geometry and the per-step copy.  The copy is cut into 1 KB slabs, one
 // per 16-byte load instruction of a wave: 8 rows of A (128 bytes each), 32
 // columns of B codes (32 bytes each); the scales take one 4-byte load per
@@ -105,7 +113,8 @@ struct Cfg {
 // workgroup size).  SJ: 16-byte scale chunks per column the workgroup may
 // preload (0: none; else the launcher guarantees at most 4 SJ K steps per
 // workgroup; see the preload below).
-template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE, int SJ = 0, bool K2 = false>
+template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE, int SJ = 0, bool K2 = false,
+          bool SK = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_gemm_a16(GemmArgs g) {
     using C = Cfg<TM, TN, WM, WN, NS>;
@@ -147,7 +156,21 @@ void k_gemm_a16(GemmArgs g) {
         id = (id & 7) * per_xcd + j;
     }
     if (id >= total) return;
+    const int ksteps = (int)(g.K / 64);
+    // Stream-K (SK: ungrouped, sk_wgs > 0): the tiles' K steps, tile after tile,
+    // are dealt out evenly, workgroup id taking global steps [sk0, sk1); it
+    // runs one pass of the body below per tile its range touches and writes
+    // that tile's part to partial slot id - sk_first(tile).
+    int64_t sk0 = 0, sk1 = 0;
+    if constexpr (SK) {
+        const int64_t S = (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * ksteps;
+        sk0 = (int64_t)id * S / g.sk_wgs;
+        sk1 = (int64_t)(id + 1) * S / g.sk_wgs;
+        if (sk0 >= sk1) return;   // (the host keeps sk_wgs <= S: never taken)
+    }
+    for (;;) {
     int grp = 0, tn, kz;
+    int kc0_, nsteps_;
     int64_t row_beg, row_end;
     if (g.groups > 0) {
         const int ntiles = g.grouped_ntiles;
@@ -163,12 +186,26 @@ void k_gemm_a16(GemmArgs g) {
         grp = lo;
         row_beg = (int64_t)g.row_off[grp] + (int64_t)(mt - g.tile_off[grp]) * BM;
         row_end = min((int64_t)g.row_off[grp + 1], row_beg + BM);
+        const int per = (ksteps + g.ksplit - 1) / g.ksplit;
+        kc0_ = kz * per;
+        nsteps_ = max(0, min(ksteps - kc0_, per));
     } else {
         const int mtiles = (int)((g.M + BM - 1) / BM);
         const int ntiles = (int)((g.N + BN - 1) / BN);
         const int per_split = mtiles * ntiles;
-        kz = id / per_split;
-        const int t = id - kz * per_split;
+        int t;
+        if constexpr (SK) {
+            t = (int)(sk0 / ksteps);
+            kc0_ = (int)(sk0 - (int64_t)t * ksteps);
+            nsteps_ = (int)min((int64_t)(ksteps - kc0_), sk1 - sk0);
+            kz = id - sk_first((int64_t)t * ksteps, g.sk_wgs, (int64_t)per_split * ksteps);
+        } else {
+            kz = id / per_split;
+            t = id - kz * per_split;
+            const int per = (ksteps + g.ksplit - 1) / g.ksplit;
+            kc0_ = kz * per;
+            nsteps_ = max(0, min(ksteps - kc0_, per));
+        }
         const int band = t / (kGroupM * ntiles);
         const int first_m = band * kGroupM;
         const int gsz = min(mtiles - first_m, kGroupM);
@@ -178,10 +215,9 @@ void k_gemm_a16(GemmArgs g) {
         row_beg = (int64_t)tm * BM;
         row_end = min(g.M, row_beg + BM);
     }
-    const int ksteps = (int)(g.K / 64);
-    const int per = (ksteps + g.ksplit - 1) / g.ksplit;
-    const int kc0 = __builtin_amdgcn_readfirstlane(kz * per);
-    int nsteps = __builtin_amdgcn_readfirstlane(max(0, min(ksteps - kc0, per)));
+    const int kc0 = __builtin_amdgcn_readfirstlane(kc0_);
+    const int seg_steps = __builtin_amdgcn_readfirstlane(nsteps_);
+    int nsteps = seg_steps;
     const int gi = g.groups > 0 ? grp : 0;
     float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
     // LoRA overlay: the accumulators start at (lora_scale / sc) * (Z Bg^T),
@@ -621,6 +657,15 @@ void k_gemm_a16(GemmArgs g) {
             }
         }
     }
+    // next stream-K segment (the K loop ended on a barrier, so the stage
+    // buffers are free; the epilogue used registers only)
+    if constexpr (!SK) {
+        break;
+    } else {
+        sk0 += seg_steps;
+        if (sk0 >= sk1) break;
+    }
+    }
 }
 
 template <int TM, int TN, int WM, int WN, int NS, AFmt AF, Epi EP, int WPE = 1, int SJ = 0, bool K2 = false>
@@ -636,6 +681,18 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
         g.grouped_ntiles = (int32_t)((ncols + bn - 1) / bn);
         wgs = (int64_t)g.grouped_ntiles * grid_m * g.ksplit;
         wgs = (wgs + 7) / 8 * 8;  // a multiple of 8 for the XCD renumbering
+    } else if (g.sk_wgs > 0) {
+        // stream-K: ungrouped partial sums with the per-step scale loads only
+        // (the scale preload and the two-step stages assume one K range per
+        // workgroup)
+        const int64_t steps = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * (g.K / 64);
+        if constexpr (EP == Epi::kPartialF32 && SJ == 0 && !K2) {
+            if (g.ksplit != 1 || g.sk_wgs > steps) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ, K2, true>), dim3((unsigned)g.sk_wgs),
+                               dim3(C::NT), 0, stream, g);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
     } else {
         wgs = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * g.ksplit;
     }
@@ -711,6 +768,60 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 #pragma unroll
             for (int k = 0; k < KS; ++k) s += p[k];
             y[v] = (uint16_t)f32_to_bf16_rne(s * scale);
+        }
+    }
+}
+
+// Stream-K finish: (m, n) lies in tile t (the kernel's band order), whose
+// K steps [t ks, (t + 1) ks) were shared by workgroups first(t) .. last(t);
+// the slots 0 .. last - first are summed in order.  V = 4 columns per thread
+// (N % 4 == 0: a thread's columns share a tile), else 1.
+constexpr int kMaxSkSlots = 8;
+template <int V>
+__global__ __launch_bounds__(256) void k_streamk_reduce(const float* __restrict__ partial, int64_t M, int64_t N,
+                                                        int ksteps, int wgs, int bm, int bn,
+                                                        const float* __restrict__ g0, const float* __restrict__ g1,
+                                                        uint16_t* __restrict__ y, bool y8) {
+    const float scale = *g0 * (g1 ? *g1 : 1.0f);
+    const int64_t total = M * N, n = total / V;
+    const int mtiles = (int)((M + bm - 1) / bm), ntiles = (int)((N + bn - 1) / bn);
+    const int64_t S = (int64_t)mtiles * ntiles * ksteps;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) {
+        const int64_t e = V * v, row = e / N, col = e - row * N;
+        const int tm = (int)(row / bm), tn = (int)(col / bn);
+        const int band = tm / kGroupM, first_m = band * kGroupM;
+        const int gsz = min(mtiles - first_m, kGroupM);
+        const int64_t t = (int64_t)band * kGroupM * ntiles + (tm - first_m) + (int64_t)gsz * tn;
+        const int w0 = sk_first(t * ksteps, wgs, S), w1 = sk_first((t + 1) * ksteps - 1, wgs, S);
+        const int slots = w1 - w0 + 1;
+        if constexpr (V == 4) {
+            f32x4 p[kMaxSkSlots];
+#pragma unroll
+            for (int k = 0; k < kMaxSkSlots; ++k)
+                if (k < slots) p[k] = *reinterpret_cast<const f32x4*>(partial + k * total + e);
+            float s[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                s[c] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kMaxSkSlots; ++k)
+                    if (k < slots) s[c] += p[k][c];
+            }
+            uint32_t b[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = f32_to_bf16_rne(s[c] * scale);
+            if (y8) {
+                *reinterpret_cast<uint2*>(y + e) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[e + c] = (uint16_t)b[c];
+            }
+        } else {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kMaxSkSlots; ++k)
+                if (k < slots) s += partial[k * total + e];
+            y[e] = (uint16_t)f32_to_bf16_rne(s * scale);
         }
     }
 }
@@ -810,6 +921,40 @@ hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int
         case 16: return launch_reduce_ks<16>(partial, total, g0, g1, y, stream);
         default: return hipErrorInvalidValue;   // the split-K plans use 2 .. 16 splits
     }
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+int streamk_slots(int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs) {
+    const int64_t bm = a16_tile_rows(tile), bn = a16_tile_cols(tile), ks = K / 64;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn), S = tiles * ks;
+    if (wgs <= 0 || ks <= 0 || wgs > S) return 0;
+    int most = 0;
+    for (int64_t t = 0; t < tiles; ++t)
+        most = std::max(most, sk_first((t + 1) * ks - 1, wgs, S) - sk_first(t * ks, wgs, S) + 1);
+    return most;
+}
+
+hipError_t launch_streamk_reduce(const float* partial, int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs,
+                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
+    const int slots = streamk_slots(M, N, K, tile, wgs);
+    if (slots < 1 || slots > kMaxSkSlots) return hipErrorInvalidValue;
+    const int bm = a16_tile_rows(tile), bn = a16_tile_cols(tile);
+    const bool vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(partial) & 15u) == 0;
+    const int64_t n = vec ? M * N / 4 : M * N;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 8192) grid = 8192;
+    if (grid < 1) grid = 1;
+    const bool y8 = (reinterpret_cast<uintptr_t>(y) & 7u) == 0;
+    if (vec)
+        hipLaunchKernelGGL((k_streamk_reduce<4>), dim3((unsigned)grid), dim3(256), 0, stream, partial, M, N,
+                           (int)(K / 64), wgs, bm, bn, g0, g1, y, y8);
+    else
+        hipLaunchKernelGGL((k_streamk_reduce<1>), dim3((unsigned)grid), dim3(256), 0, stream, partial, M, N,
+                           (int)(K / 64), wgs, bm, bn, g0, g1, y, y8);
+    return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -144,6 +144,12 @@ struct GemmArgs {
     uint16_t* out_q = nullptr;
     const float* q_global = nullptr;
     int32_t ksplit = 1;
+    // stream-K (ungrouped kPartialF32, ksplit 1): the mtiles ntiles (K / 64)
+    // K steps, tile after tile, are dealt evenly to sk_wgs workgroups; the
+    // part of tile t done by workgroup w goes to partial slot w - first(t)
+    // (first(t): the workgroup holding the tile's first step), summed by
+    // launch_streamk_reduce.  0: the ksplit layout.
+    int32_t sk_wgs = 0;
     int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
     // LoRA overlay (the kMoe*Lora epilogues, ksplit 1): the
     // epilogue value of (row, col) becomes
@@ -180,14 +186,22 @@ int a16_tile_cols(A16Tile t);
 hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, int grid_m,
                            hipStream_t stream);
 
-// y[m, n] = bf16(scale * sum_s partial[s][m][n]), scale = *g0 * (g1 ? *g1 : 1)
 // Rank-r projection of LoRA's shared A (lora.hip): Z [rows, R] =
 // bf16(X [rows, K] * A [R, K]^T) with fp32 accumulation; K % 64 == 0,
 // R % 8 == 0, R <= 128.
 hipError_t launch_lora_a(const uint16_t* x, int64_t rows, int64_t K, const uint16_t* a, int R, uint16_t* z,
                          hipStream_t stream);
+// y[m, n] = bf16(scale * sum_s partial[s][m][n]), scale = *g0 * (g1 ? *g1 : 1)
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N,
                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
+// Stream-K on the ungrouped tile `tile`: the most partial slots one tile
+// takes with `wgs` workgroups (the partial buffer holds that many [M, N]
+// slots), or 0 when wgs exceeds the K steps of the problem.
+int streamk_slots(int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs);
+// The stream-K finish: y[m, n] = bf16(scale * sum over the slots of the tile
+// holding (m, n), in slot order), scale as for launch_splitk_reduce.
+hipError_t launch_streamk_reduce(const float* partial, int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs,
+                                 const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
 
 // ------------------------------------------------------- small-batch stream --
 

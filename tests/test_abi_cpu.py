@@ -137,6 +137,12 @@ def test_gemm_w4a16_validation():
     assert L.nvfp4_gemm_w4a16_workspace_size(4096, 16384, 2048) == 0   # 1024 tiles, no split
     # o_proj at M = 4096: 384 tiles of 256 x 256, K split in two (two fp32 partials)
     assert L.nvfp4_gemm_w4a16_workspace_size(4096, 6144, 16384) == 2 * 4096 * 6144 * 4
+    # M = 1536: 144 tiles, stream-K over 256 workgroups of 144 * 256 / 256 =
+    # 144 K steps each; a tile's 256 steps meet at most 3 workgroups (3 slots)
+    assert L.nvfp4_gemm_w4a16_workspace_size(1536, 6144, 16384) == 3 * 1536 * 6144 * 4
+    # M = 1024, N = 5632, K = 8192: 88 tiles of 128 steps, 44 steps a
+    # workgroup, so a tile spans at most 4 workgroups
+    assert L.nvfp4_gemm_w4a16_workspace_size(1024, 5632, 8192) == 4 * 1024 * 5632 * 4
     assert g(None, 128, 256, 4096, A, A, A, A, A, ws, None) == NULL
     assert g(A, 128, 256, 4100, A, A, A, A, A, ws, None) == SHAPE
     assert g(A, 128, 256, 4128, A, A, A, A, A, 1 << 30, None) == UNSUP   # K % 64 != 0

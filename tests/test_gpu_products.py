@@ -142,6 +142,33 @@ def test_gemm_long_row_splits(orc, M, N, K):
                  f"gemm w4a16 {M}x{N}x{K}")
 
 
+# long rows where the one-per-CU split leaves most CUs idle take stream-K:
+# 256 workgroups share the tiles' K steps evenly, so a tile's K range is cut
+# at arbitrary steps into parts summed afterwards.  (1400, 6001, 4160): 144
+# tiles of 65 K steps, 36.6 steps per workgroup, N odd (the finish's
+# one-column-per-thread path), ragged row and column tiles; (1536, 5888,
+# 4352): 138 tiles; (1700, 5000, 16384): 140 tiles of 256 steps; (1024,
+# 5632, 8192): 88 tiles otherwise split 2, up to 4 parts per tile.  Every
+# 256 x 256 tile is sampled.
+@pytest.mark.parametrize("M,N,K", [(1400, 6001, 4160), (1536, 5888, 4352), (1700, 5000, 16384), (1024, 5632, 8192)])
+def test_gemm_stream_k(orc, M, N, K):
+    w = wl.layer_weight((N, K), seed=M + 3 * N)
+    x = wl.activations(M, K, seed=M * 7 + K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    y16 = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    rng = np.random.default_rng(M + N + K)
+    rows = np.unique(np.concatenate([np.minimum(M - 1, r0 + rng.choice(256, 6, replace=False))
+                                     for r0 in range(0, M, 256)] + [[0, M - 1]]))
+    cols = np.unique(np.concatenate([np.minimum(N - 1, c0_ + rng.choice(256, 4, replace=False))
+                                     for c0_ in range(0, N, 256)] + [[0, N - 1]]))
+    assert_close(y[np.ix_(rows, cols)], orc.gemm_w4a4(x[rows], isc, c0[cols], s0[cols], g0),
+                 f"gemm stream-K {M}x{N}x{K}")
+    assert_close(y16[np.ix_(rows, cols)], orc.gemv_w4a16(x[rows], c0[cols], s0[cols], g0),
+                 f"gemm w4a16 stream-K {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("name", ["o_proj", "q_b_proj"])
 @pytest.mark.parametrize("M", list(wl.GEMM_M_SWEEP))
 def test_gemm_layers_sampled(orc, name, M):
