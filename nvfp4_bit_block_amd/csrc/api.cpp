@@ -117,21 +117,28 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16_a = false) {
     if ((p.tile == A16Tile::k128x128_w64x64 || p.tile == A16Tile::k256x256_w128x64) && p.ksplit == 1 &&
         tiles >= 256 && tiles < 512 && ksteps >= 128)
         p.ksplit = 2;
-    // Stream-K where the one-per-CU split leaves many CUs idle: 256
-    // workgroups share the tiles' K steps evenly, each tile's parts summed in
-    // order afterwards.  The chip does not run 256 busy CUs much faster than
-    // 192, and the finish reads every part, so it pays only below about 70 %
-    // of the CUs (measured on MI355X, o_proj 6144 x 16384, f16 / bf16
-    // activation: M = 1536, 144 workgroups unsplit, 359.7 / 376.2 -> 306.6 /
-    // 319.0 us; M = 1024, 192 at split 2, 227.5 / 227.5 -> 222.2 / 223.8; M =
-    // 2048, 192 unsplit, 382.0 / 417.4 -> 387.2 / 407.0; M = 768, 216 at
-    // split 3, 156.7 / 166.8 -> 161.6 / 173.3).  One launch (the rows fit
-    // one buffer resource), at least 8 K steps per workgroup.
-    if (one_per_cu && tiles * p.ksplit <= 176 && gemm_chunk_rows(M, K) >= M && tiles * ksteps >= 256 * 8) {
+    // Stream-K for the 256 x 256 tile on long rows: 256 workgroups share the
+    // tiles' K steps evenly, a workgroup holding a whole tile writes it
+    // finished, and the other tiles' parts are summed in order afterwards.
+    // The chip does not run 256 busy CUs much faster than 192, and the
+    // finish reads every part, so below 256 tiles it pays only where the
+    // split leaves about 30 % of the CUs idle (measured on MI355X, o_proj
+    // 6144 x 16384, f16 / bf16 activation: M = 1536, 144 workgroups
+    // unsplit, 359.7 / 376.2 -> 306.6 / 319.0 us; M = 1024, 192 at split 2,
+    // 227.5 / 227.5 -> 222.2 / 223.8; M = 2048, 192 unsplit, 382.0 / 417.4
+    // -> 387.2 / 407.0; M = 768, 216 at split 3, 156.7 / 166.8 -> 161.6 /
+    // 173.3).  With 256-511 tiles it replaces split 2 (same box, four runs
+    // each: M = 4096 696.8 / 742.2 -> 681.6 / 727.5 us, M = 3072 604.0 /
+    // 656.2 -> 582.8 / 618.3; on short rows, q_b_proj's 1024 tiles of 32
+    // steps, it lost 4-6 % to the plain grid).  One launch (the rows fit one
+    // buffer resource), at least 8 K steps per workgroup.
+    const bool sk_idle = tiles * p.ksplit <= 176;
+    const bool sk_rounds = tiles >= 256 && tiles < 512 && ksteps >= 128;
+    if (one_per_cu && (sk_idle || sk_rounds) && gemm_chunk_rows(M, K) >= M && tiles * ksteps >= 256 * 8) {
         const int slots = streamk_slots(M, N, K, p.tile, 256);
-        if (slots >= 2 && slots <= 8) {
+        if (slots >= 1 && slots <= 8) {
             p.sk_wgs = 256;
-            p.ksplit = slots;
+            p.ksplit = slots;   // partial slots (one: every tile is written whole)
         }
     }
     return p;
@@ -336,6 +343,7 @@ hipError_t run_gemm_tiles(const GemmPlan& p, const uint16_t* a, AFmt afmt, const
         if (p.sk_wgs > 0) {
             g.ksplit = 1;
             g.sk_wgs = p.sk_wgs;
+            g.sk_y = y + r0 * N;
             g.out = partial;
             g.ldo = N;
             e = launch_gemm_a16(g, afmt, Epi::kPartialF32, p.tile, 0, s);

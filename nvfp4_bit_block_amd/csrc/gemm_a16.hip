@@ -160,7 +160,8 @@ void k_gemm_a16(GemmArgs g) {
     // Stream-K (SK: ungrouped, sk_wgs > 0): the tiles' K steps, tile after tile,
     // are dealt out evenly, workgroup id taking global steps [sk0, sk1); it
     // runs one pass of the body below per tile its range touches and writes
-    // that tile's part to partial slot id - sk_first(tile).
+    // that tile's part to partial slot id - sk_first(tile), or, when it holds
+    // the whole tile, the finished bf16 tile to sk_y.
     int64_t sk0 = 0, sk1 = 0;
     if constexpr (SK) {
         const int64_t S = (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * ksteps;
@@ -218,6 +219,7 @@ void k_gemm_a16(GemmArgs g) {
     const int kc0 = __builtin_amdgcn_readfirstlane(kc0_);
     const int seg_steps = __builtin_amdgcn_readfirstlane(nsteps_);
     int nsteps = seg_steps;
+    const bool sk_whole = SK && kc0 == 0 && seg_steps == ksteps;
     const int gi = g.groups > 0 ? grp : 0;
     float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
     // LoRA overlay: the accumulators start at (lora_scale / sc) * (Z Bg^T),
@@ -649,7 +651,10 @@ void k_gemm_a16(GemmArgs g) {
                     if constexpr (EP == Epi::kStoreBf16) {
                         reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(v * sc);
                     } else if constexpr (EP == Epi::kPartialF32) {
-                        reinterpret_cast<float*>(g.out)[((int64_t)kz * g.M + row) * g.ldo + col] = v;
+                        if (sk_whole)
+                            g.sk_y[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(v * sc);
+                        else
+                            reinterpret_cast<float*>(g.out)[((int64_t)kz * g.M + row) * g.ldo + col] = v;
                     } else {
                         reinterpret_cast<float*>(g.out)[row * g.ldo + col] = v * sc;
                     }
@@ -687,7 +692,7 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
         // workgroup)
         const int64_t steps = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * (g.K / 64);
         if constexpr (EP == Epi::kPartialF32 && SJ == 0 && !K2) {
-            if (g.ksplit != 1 || g.sk_wgs > steps) return hipErrorInvalidValue;
+            if (g.ksplit != 1 || g.sk_wgs > steps || g.sk_y == nullptr) return hipErrorInvalidValue;
             hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ, K2, true>), dim3((unsigned)g.sk_wgs),
                                dim3(C::NT), 0, stream, g);
             return hipGetLastError();
@@ -774,7 +779,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 // Stream-K finish: (m, n) lies in tile t (the kernel's band order), whose
 // K steps [t ks, (t + 1) ks) were shared by workgroups first(t) .. last(t);
-// the slots 0 .. last - first are summed in order.  V = 4 columns per thread
+// the slots 0 .. last - first are summed in order (a tile of one slot was
+// finished by the GEMM).  V = 4 columns per thread
 // (N % 4 == 0: a thread's columns share a tile), else 1.
 constexpr int kMaxSkSlots = 8;
 template <int V>
@@ -794,6 +800,7 @@ __global__ __launch_bounds__(256) void k_streamk_reduce(const float* __restrict_
         const int64_t t = (int64_t)band * kGroupM * ntiles + (tm - first_m) + (int64_t)gsz * tn;
         const int w0 = sk_first(t * ksteps, wgs, S), w1 = sk_first((t + 1) * ksteps - 1, wgs, S);
         const int slots = w1 - w0 + 1;
+        if (slots == 1) continue;   // written whole by the GEMM
         if constexpr (V == 4) {
             f32x4 p[kMaxSkSlots];
 #pragma unroll
@@ -941,6 +948,7 @@ hipError_t launch_streamk_reduce(const float* partial, int64_t M, int64_t N, int
                                  const float* g0, const float* g1, uint16_t* y, hipStream_t stream) {
     const int slots = streamk_slots(M, N, K, tile, wgs);
     if (slots < 1 || slots > kMaxSkSlots) return hipErrorInvalidValue;
+    if (slots == 1) return hipSuccess;   // every tile was finished by the GEMM
     const int bm = a16_tile_rows(tile), bn = a16_tile_cols(tile);
     const bool vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(partial) & 15u) == 0;
     const int64_t n = vec ? M * N / 4 : M * N;

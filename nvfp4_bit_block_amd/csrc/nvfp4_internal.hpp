@@ -148,8 +148,11 @@ struct GemmArgs {
     // K steps, tile after tile, are dealt evenly to sk_wgs workgroups; the
     // part of tile t done by workgroup w goes to partial slot w - first(t)
     // (first(t): the workgroup holding the tile's first step), summed by
-    // launch_streamk_reduce.  0: the ksplit layout.
+    // launch_streamk_reduce; a tile done whole by one workgroup is written
+    // straight to sk_y (bf16 [M, ldo], scaled) and the finish skips it.
+    // 0: the ksplit layout.
     int32_t sk_wgs = 0;
+    uint16_t* sk_y = nullptr;
     int64_t half_n = 0;  // gate/up epilogue: I (the up rows start at I)
     // LoRA overlay (the kMoe*Lora epilogues, ksplit 1): the
     // epilogue value of (row, col) becomes
@@ -199,7 +202,8 @@ hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int
 // slots), or 0 when wgs exceeds the K steps of the problem.
 int streamk_slots(int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs);
 // The stream-K finish: y[m, n] = bf16(scale * sum over the slots of the tile
-// holding (m, n), in slot order), scale as for launch_splitk_reduce.
+// holding (m, n), in slot order), scale as for launch_splitk_reduce; tiles
+// of one slot were written by the GEMM itself and are left alone.
 hipError_t launch_streamk_reduce(const float* partial, int64_t M, int64_t N, int64_t K, A16Tile tile, int wgs,
                                  const float* g0, const float* g1, uint16_t* y, hipStream_t stream);
 

@@ -142,15 +142,19 @@ def test_gemm_long_row_splits(orc, M, N, K):
                  f"gemm w4a16 {M}x{N}x{K}")
 
 
-# long rows where the one-per-CU split leaves most CUs idle take stream-K:
-# 256 workgroups share the tiles' K steps evenly, so a tile's K range is cut
-# at arbitrary steps into parts summed afterwards.  (1400, 6001, 4160): 144
-# tiles of 65 K steps, 36.6 steps per workgroup, N odd (the finish's
-# one-column-per-thread path), ragged row and column tiles; (1536, 5888,
-# 4352): 138 tiles; (1700, 5000, 16384): 140 tiles of 256 steps; (1024,
-# 5632, 8192): 88 tiles otherwise split 2, up to 4 parts per tile.  Every
-# 256 x 256 tile is sampled.
-@pytest.mark.parametrize("M,N,K", [(1400, 6001, 4160), (1536, 5888, 4352), (1700, 5000, 16384), (1024, 5632, 8192)])
+# Long rows on the 256 x 256 tile take stream-K where the one-per-CU split
+# leaves most CUs idle, and with 256-511 tiles: 256 workgroups share the
+# tiles' K steps evenly, so a tile's K range is cut at arbitrary steps into
+# parts summed afterwards, and a tile held whole by one workgroup is written
+# by the GEMM.  (1400, 6001, 4160): 144 tiles of 65 K steps, 36.6 steps per
+# workgroup, N odd (the finish's one-column-per-thread path), ragged row and
+# column tiles; (1536, 5888, 4352): 138 tiles; (1700, 5000, 16384): 140
+# tiles of 256 steps; (1024, 5632, 8192): 88 tiles otherwise split 2, up to
+# 4 parts per tile; (3000, 6000, 8320): 288 tiles of 130 steps, 146.25 per
+# workgroup, so some tiles whole and the rest in two parts.  Every 256 x 256
+# tile is sampled.
+@pytest.mark.parametrize("M,N,K", [(1400, 6001, 4160), (1536, 5888, 4352), (1700, 5000, 16384), (1024, 5632, 8192),
+                                   (3000, 6000, 8320)])
 def test_gemm_stream_k(orc, M, N, K):
     w = wl.layer_weight((N, K), seed=M + 3 * N)
     x = wl.activations(M, K, seed=M * 7 + K)
