@@ -367,11 +367,19 @@ hipError_t run_gemm_tiles(const GemmPlan& p, const uint16_t* a, AFmt afmt, const
 
 // ------------------------------------------------------------ MoE planning --
 
-// Row tile of the grouped GEMMs (a group's rows are covered by tiles of this
-// height; measured on MI355X, 128-row tiles at three workgroups per CU beat
-// 160- and 256-row tiles that read each expert's weights only once but run
-// one wave per SIMD).
-constexpr int kMoeBM = 128;
+// Row tile of the grouped GEMMs: a group's rows are covered by tiles of this
+// height, multiplied by four waves of 96 x 64 (a tile of at most 128 rows
+// splits them 64 / 64 between its wave rows).  With about 128 rows per
+// expert, 128-row tiles give half the experts a second tile of a few rows
+// that still loads and decodes the expert's whole weight tile (with every
+// expert at exactly 128 rows the layer took 3.4 ms against 4.2 ms on the
+// benchmark's routing of 103-157 rows); 192-row tiles hold every such
+// expert in one (measured on MI355X, benchmark routing, random NVFP4
+// experts: W4A16 4.21-4.44 -> 3.78-3.88 ms, W4A4 4.10-4.25 -> 3.78 ms,
+// bit-identical; with every expert at exactly 128 rows 3.39 / 3.30 ->
+// 3.62 / 3.80 ms).  Earlier 192-row tiles of six 64 x 64 waves decoded each
+// weight tile three times and lost (5.3 ms).
+constexpr int kMoeBM = 192;
 
 struct MoeLayout {
     size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0, route = 0;
@@ -848,7 +856,7 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
     // GEMM 1: [g | u] = x^ W13^T, h = bf16(silu(g) * u).  W4A16 multiplies the
     // bf16 tokens (gathered by slot); W4A4 first quantizes them per expert
     // group under a13_scale into their exact f16 products q * s.
-    const A16Tile tile = A16Tile::k128x128_w64x64;  // kMoeBM-row tiles, as the routing counted
+    const A16Tile tile = A16Tile::k192x128_w96x64;  // kMoeBM-row tiles, as the routing counted
     GemmArgs g1;
     g1.b_codes = t->w13_codes;
     g1.b_scales = t->w13_scales;

@@ -221,6 +221,14 @@ void k_gemm_a16(GemmArgs g) {
     int nsteps = seg_steps;
     const bool sk_whole = SK && kc0 == 0 && seg_steps == ksteps;
     const int gi = g.groups > 0 ? grp : 0;
+    // First row of the wave within the tile.  Grouped tiles of 96-row waves
+    // (TM = 3) whose rows fit two 64-row halves (an expert of at most
+    // 2 x 64 rows) give each wave row 64 of them, so that no wave decodes
+    // the weights for a single 32-row block; tm_cap is then 2.
+    constexpr bool kDynRows = TM == 3 && EP != Epi::kStoreBf16 && EP != Epi::kPartialF32;
+    const bool half_rows = kDynRows && row_end - row_beg <= 64 * WM;
+    const int wrow = half_rows ? wm * 64 : wm * WTM;
+    const int tm_cap = half_rows ? 2 : TM;
     float sc = (g.a_global ? g.a_global[gi] : 1.0f) * (g.b_global ? g.b_global[gi] : 1.0f);
     // LoRA overlay: the accumulators start at (lora_scale / sc) * (Z Bg^T),
     // so that the epilogue's sc * acc adds lora_scale * (Z Bg^T) to the
@@ -288,7 +296,7 @@ void k_gemm_a16(GemmArgs g) {
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int64_t row = row_beg + wm * WTM + 32 * i + c32;
+            const int64_t row = row_beg + wrow + 32 * i + c32;
             zp[i] = nullptr;
             if (row < row_end)
                 zp[i] = g.lora_z + (int64_t)(g.lora_rows ? g.lora_rows[row] / g.lora_div : (int32_t)row) * R + 8 * hf;
@@ -416,7 +424,7 @@ void k_gemm_a16(GemmArgs g) {
     uint32_t fa_k[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        fa_k[kk] = (uint32_t)((wm * WTM + c32) * 128 + 16 * ((4 * hf + kk) ^ ((c32 >> 1) & 7)));
+        fa_k[kk] = (uint32_t)((wrow + c32) * 128 + 16 * ((4 * hf + kk) ^ ((c32 >> 1) & 7)));
     const uint32_t fbc0 = (uint32_t)(C::A_BYTES + (wn * WTN + c32) * 32 + 16 * (hf ^ ((c32 >> 3) & 1)));
     const uint32_t fbs0 = (uint32_t)(C::A_BYTES + C::B_BYTES + 4 * (wn * WTN + c32));
     auto fa = [&](int i, int kk) { return fa_k[kk] + 32 * 128 * i; };
@@ -429,11 +437,12 @@ void k_gemm_a16(GemmArgs g) {
     // just in time to save registers and the MFMAs wait on LDS latency).
     // Waves whose rows all lie past the end of the row tile (a group's last,
     // partly filled tile) skip their MFMAs; the copy work stays shared.
-    const bool wave_rows = (int64_t)wm * WTM < row_end - row_beg;
-    // Grouped tiles: a wave whose rows past the first 32 are all padding
-    // skips the MFMAs of its second 32-row block.
-    constexpr bool kHalfSkip = TM == 2 && EP != Epi::kStoreBf16 && EP != Epi::kPartialF32;
-    const bool wave_half = kHalfSkip && (int64_t)wm * WTM + 32 >= row_end - row_beg;
+    const bool wave_rows = (int64_t)wrow < row_end - row_beg;
+    // Grouped tiles: a wave skips the MFMAs of its 32-row blocks that hold
+    // only padding (wave_blocks: the blocks with at least one real row).
+    constexpr bool kBlockSkip = (TM == 2 || TM == 3) && EP != Epi::kStoreBf16 && EP != Epi::kPartialF32;
+    const int wave_blocks =
+        kBlockSkip ? (int)min((int64_t)tm_cap, (row_end - row_beg - (int64_t)wrow + 31) / 32) : TM;
     const int gsc = (c32 >> 1) & (sj > 0 ? sj - 1 : 0);
     // (the tile's column offsets wn WTN + 32 j are multiples of 32, so the
     // slot permutation of column wn WTN + 32 j + c32 depends on c32 alone)
@@ -507,7 +516,7 @@ void k_gemm_a16(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
-                    if (i > 0 && wave_half) break;
+                    if (i > 0 && i >= wave_blocks) break;
 #pragma unroll
                     for (int j = 0; j < TN; ++j) acc[i][j] = mfma(av[kk & 1][i], bv[j], acc[i][j]);
                 }
@@ -617,9 +626,10 @@ void k_gemm_a16(GemmArgs g) {
     const float tq = 6.0f * sgq;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        if (i >= tm_cap) break;   // (64-row halves: the third block is the next wave's)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t row = row_beg + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const int64_t row = row_beg + wrow + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
             // (the row depends on the lane only through hf, so the 16-lane
             // groups of the gate/up quantization below stay whole)
             if (row >= row_end) continue;
@@ -730,6 +740,7 @@ hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t 
         case A16Tile::k128x128_w32x64: return launch_small<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
         case A16Tile::k64x256_w64x64: return launch_small<2, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
         case A16Tile::k32x256_w32x64: return launch_small<1, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
+        case A16Tile::k192x128_w96x64: return launch_cfg<3, 2, 2, 2, 2, AF, EP, 2>(g, grid_m, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -864,6 +875,7 @@ int a16_tile_rows(A16Tile t) {
         case A16Tile::k128x128_w32x64: return 128;
         case A16Tile::k64x256_w64x64: return 64;
         case A16Tile::k32x256_w32x64: return 32;
+        case A16Tile::k192x128_w96x64: return 192;
     }
     return 0;
 }
@@ -879,6 +891,7 @@ int a16_tile_cols(A16Tile t) {
         case A16Tile::k128x128_w32x64: return 128;
         case A16Tile::k64x256_w64x64: return 256;
         case A16Tile::k32x256_w32x64: return 256;
+        case A16Tile::k192x128_w96x64: return 128;
     }
     return 0;
 }
@@ -892,11 +905,11 @@ hipError_t launch_gemm_a16(const GemmArgs& g, AFmt afmt, Epi epi, A16Tile tile, 
         case Epi::kMoeGateUp: return launch_tile<AF, Epi::kMoeGateUp>(g, tile, grid_m, stream);   \
         case Epi::kMoeDown: return launch_tile<AF, Epi::kMoeDown>(g, tile, grid_m, stream);       \
         case Epi::kMoeGateUpLora:                                                         \
-            if (tile != A16Tile::k128x128_w64x64) break;                                  \
-            return launch_cfg<2, 2, 2, 2, 2, AF, Epi::kMoeGateUpLora, 3>(g, grid_m, stream); \
+            if (tile != A16Tile::k192x128_w96x64) break;                                  \
+            return launch_cfg<3, 2, 2, 2, 2, AF, Epi::kMoeGateUpLora, 2>(g, grid_m, stream); \
         case Epi::kMoeDownLora:                                                           \
-            if (tile != A16Tile::k128x128_w64x64) break;                                  \
-            return launch_cfg<2, 2, 2, 2, 2, AF, Epi::kMoeDownLora, 3>(g, grid_m, stream);   \
+            if (tile != A16Tile::k192x128_w96x64) break;                                  \
+            return launch_cfg<3, 2, 2, 2, 2, AF, Epi::kMoeDownLora, 2>(g, grid_m, stream);   \
     }
     switch (afmt) {
         case AFmt::kF16: NVFP4_EPI(AFmt::kF16) break;

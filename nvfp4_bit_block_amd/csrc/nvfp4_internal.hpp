@@ -180,6 +180,7 @@ enum class A16Tile : int {
     k128x128_w32x64 = 6,
     k64x256_w64x64 = 7,
     k32x256_w32x64 = 8,
+    k192x128_w96x64 = 9,
 };
 int a16_tile_rows(A16Tile t);
 // Each operand of launch_gemm_a16 is addressed through one buffer resource
