@@ -88,9 +88,10 @@ __host__ __device__ __forceinline__ int sk_first(int64_t x, int W, int64_t S) {
 // Tile geometry and the per-step copy.  The copy is cut into 1 KB slabs, one
 // per 16-byte load instruction of a wave: 8 rows of A (128 bytes each), 32
 // columns of B codes (32 bytes each); the scales take one 4-byte load per
-// 64 columns.  Every wave issues the same number of loads per step (waves
-// without a B or scale slab load past the end of the buffer, which writes
-// zeros to an unused slab), so that the vmcnt waits are exact.
+// 64 columns.  With three or more stages every wave issues the same number
+// of loads per step (waves without a B or scale slab load past the end of
+// the buffer, which writes zeros to an unused slab), so that the vmcnt waits
+// are exact; with two stages each step waits for all of its loads.
 template <int TM, int TN, int WM, int WN, int NS>
 struct Cfg {
     static constexpr int NW = WM * WN, NT = 64 * NW;
@@ -406,11 +407,19 @@ void k_gemm_a16(GemmArgs g) {
         for (int u = 0; u < B2_PER_W; ++u)
             lds_load16(rb_c, vbc2[u], (uint32_t)(kc0 + 2 * kg) * 32u, b + (uint32_t)(2 * C::A_BYTES + (B2_PER_W * wave + u) * 1024));
     };
+    // With two stages every step waits for all of its loads, so a wave may
+    // skip the A slabs that lie wholly past the tile's last row (their LDS
+    // rows then hold stale data, which only padding rows multiply and which
+    // the epilogue never stores).
+    bool a_live[C::A_PER_W];
+#pragma unroll
+    for (int u = 0; u < C::A_PER_W; ++u)
+        a_live[u] = NS > 2 || (int64_t)8 * (C::A_PER_W * wave + u) < row_end - row_beg;
     auto issue = [&](int kc, int st) {
         const uint32_t b = lds0 + (uint32_t)(st * C::STAGE);
 #pragma unroll
         for (int u = 0; u < C::A_PER_W; ++u)
-            lds_load16(ra, va[u], (uint32_t)kc * 128u, b + (uint32_t)((C::A_PER_W * wave + u) * 1024));
+            if (a_live[u]) lds_load16(ra, va[u], (uint32_t)kc * 128u, b + (uint32_t)((C::A_PER_W * wave + u) * 1024));
 #pragma unroll
         for (int u = 0; u < C::B_PER_W; ++u)
             lds_load16(rb_c, vbc[u], (uint32_t)kc * 32u, b + (uint32_t)(C::A_BYTES + (C::B_PER_W * wave + u) * 1024));
