@@ -797,46 +797,85 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
     }
 }
 
-// Stream-K finish: (m, n) lies in tile t (the kernel's band order), whose
-// K steps [t ks, (t + 1) ks) were shared by workgroups first(t) .. last(t);
-// the slots 0 .. last - first are summed in order (a tile of one slot was
-// finished by the GEMM).  V = 4 columns per thread
-// (N % 4 == 0: a thread's columns share a tile), else 1.
+// Stream-K finish.  Only tiles that a workgroup boundary cuts have parts to
+// sum: the start x = floor(w S / wgs) of workgroup w (1 <= w < wgs) lies
+// strictly inside tile t = x / ks.  Workgroup b of the launch takes boundary
+// w = b / pieces + 1 and kSkRows rows (piece b % pieces) of that tile; when
+// several boundaries cut one tile, the first of them does the work.  The
+// tile's (tm, tn) follow the GEMM's band order; its K steps [t ks,
+// (t + 1) ks) were shared by workgroups first(t) .. last(t), whose slots
+// 0 .. last - first are summed in order.  V = 4 columns per thread (N % 4 ==
+// 0, so a thread's columns lie in one row), else 1.
 constexpr int kMaxSkSlots = 8;
+constexpr int kSkRows = 32;
+constexpr int kSkCols = 256;   // the tile width this finish is written for
 template <int V>
 __global__ __launch_bounds__(256) void k_streamk_reduce(const float* __restrict__ partial, int64_t M, int64_t N,
-                                                        int ksteps, int wgs, int bm, int bn,
+                                                        int ksteps, int wgs, int bm,
                                                         const float* __restrict__ g0, const float* __restrict__ g1,
                                                         uint16_t* __restrict__ y, bool y8) {
-    const float scale = *g0 * (g1 ? *g1 : 1.0f);
-    const int64_t total = M * N, n = total / V;
-    const int mtiles = (int)((M + bm - 1) / bm), ntiles = (int)((N + bn - 1) / bn);
+    constexpr int kTpr = kSkCols / V;              // threads per tile row
+    constexpr int kPasses = kSkRows * kTpr / 256;  // rows per thread
+    const int mtiles = (int)((M + bm - 1) / bm), ntiles = (int)((N + kSkCols - 1) / kSkCols);
     const int64_t S = (int64_t)mtiles * ntiles * ksteps;
-    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) {
-        const int64_t e = V * v, row = e / N, col = e - row * N;
-        const int tm = (int)(row / bm), tn = (int)(col / bn);
-        const int band = tm / kGroupM, first_m = band * kGroupM;
-        const int gsz = min(mtiles - first_m, kGroupM);
-        const int64_t t = (int64_t)band * kGroupM * ntiles + (tm - first_m) + (int64_t)gsz * tn;
-        const int w0 = sk_first(t * ksteps, wgs, S), w1 = sk_first((t + 1) * ksteps - 1, wgs, S);
-        const int slots = w1 - w0 + 1;
-        if (slots == 1) continue;   // written whole by the GEMM
+    const int pieces = bm / kSkRows;
+    const int bw = (int)(blockIdx.x / (unsigned)pieces) + 1, piece = (int)(blockIdx.x % (unsigned)pieces);
+    const int64_t x = (int64_t)bw * S / wgs;
+    if (x % ksteps == 0) return;                         // between two tiles
+    const int t = (int)(x / ksteps);
+    if ((int64_t)(bw - 1) * S / wgs > (int64_t)t * ksteps) return;   // an earlier boundary cuts this tile
+    const int w0 = sk_first((int64_t)t * ksteps, wgs, S), w1 = sk_first((int64_t)(t + 1) * ksteps - 1, wgs, S);
+    const int slots = w1 - w0 + 1;
+    const int band = t / (kGroupM * ntiles), first_m = band * kGroupM;
+    const int gsz = min(mtiles - first_m, kGroupM);
+    const int r = t - band * kGroupM * ntiles;
+    const int tm = first_m + r % gsz, tn = r / gsz;
+    const float scale = *g0 * (g1 ? *g1 : 1.0f);
+    const int64_t total = M * N;
+    const int64_t col = (int64_t)tn * kSkCols + (int)(threadIdx.x % kTpr) * V;
+    if (col >= N) return;
+    const int64_t row0 = (int64_t)tm * bm + piece * kSkRows + threadIdx.x / kTpr;
+    constexpr int kRowStep = 256 / kTpr;
+    // all rows' loads of one slot are issued before they are added
+    float sum[kPasses][V];
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps)
+#pragma unroll
+        for (int c = 0; c < V; ++c) sum[ps][c] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxSkSlots; ++k) {
+        if (k >= slots) break;
         if constexpr (V == 4) {
-            f32x4 p[kMaxSkSlots];
+            f32x4 v[kPasses];
 #pragma unroll
-            for (int k = 0; k < kMaxSkSlots; ++k)
-                if (k < slots) p[k] = *reinterpret_cast<const f32x4*>(partial + k * total + e);
-            float s[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                s[c] = 0.0f;
-#pragma unroll
-                for (int k = 0; k < kMaxSkSlots; ++k)
-                    if (k < slots) s[c] += p[k][c];
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int64_t row = row0 + ps * kRowStep;
+                v[ps] = row < M ? *reinterpret_cast<const f32x4*>(partial + k * total + row * N + col) : f32x4{0, 0, 0, 0};
             }
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sum[ps][c] += v[ps][c];
+        } else {
+            float v[kPasses];
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int64_t row = row0 + ps * kRowStep;
+                v[ps] = row < M ? partial[k * total + row * N + col] : 0.0f;
+            }
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps) sum[ps][0] += v[ps];
+        }
+    }
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int64_t row = row0 + ps * kRowStep;
+        if (row >= M) break;
+        const int64_t e = row * N + col;
+        if constexpr (V == 4) {
             uint32_t b[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = f32_to_bf16_rne(s[c] * scale);
+            for (int c = 0; c < 4; ++c) b[c] = f32_to_bf16_rne(sum[ps][c] * scale);
             if (y8) {
                 *reinterpret_cast<uint2*>(y + e) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
             } else {
@@ -844,11 +883,7 @@ __global__ __launch_bounds__(256) void k_streamk_reduce(const float* __restrict_
                 for (int c = 0; c < 4; ++c) y[e + c] = (uint16_t)b[c];
             }
         } else {
-            float s = 0.0f;
-#pragma unroll
-            for (int k = 0; k < kMaxSkSlots; ++k)
-                if (k < slots) s += partial[k * total + e];
-            y[e] = (uint16_t)f32_to_bf16_rne(s * scale);
+            y[e] = (uint16_t)f32_to_bf16_rne(sum[ps][0] * scale);
         }
     }
 }
@@ -972,18 +1007,17 @@ hipError_t launch_streamk_reduce(const float* partial, int64_t M, int64_t N, int
     if (slots < 1 || slots > kMaxSkSlots) return hipErrorInvalidValue;
     if (slots == 1) return hipSuccess;   // every tile was finished by the GEMM
     const int bm = a16_tile_rows(tile), bn = a16_tile_cols(tile);
+    if (bm % kSkRows != 0 || bn != kSkCols || wgs < 2) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)(wgs - 1) * (bm / kSkRows);
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     const bool vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(partial) & 15u) == 0;
-    const int64_t n = vec ? M * N / 4 : M * N;
-    int64_t grid = (n + 255) / 256;
-    if (grid > 8192) grid = 8192;
-    if (grid < 1) grid = 1;
     const bool y8 = (reinterpret_cast<uintptr_t>(y) & 7u) == 0;
     if (vec)
         hipLaunchKernelGGL((k_streamk_reduce<4>), dim3((unsigned)grid), dim3(256), 0, stream, partial, M, N,
-                           (int)(K / 64), wgs, bm, bn, g0, g1, y, y8);
+                           (int)(K / 64), wgs, bm, g0, g1, y, y8);
     else
         hipLaunchKernelGGL((k_streamk_reduce<1>), dim3((unsigned)grid), dim3(256), 0, stream, partial, M, N,
-                           (int)(K / 64), wgs, bm, bn, g0, g1, y, y8);
+                           (int)(K / 64), wgs, bm, g0, g1, y, y8);
     return hipGetLastError();
 }
 
