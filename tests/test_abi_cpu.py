@@ -199,3 +199,32 @@ def test_moe_lora_validation():
     assert run(p, t, nv.MoeLora(64, 1.0, None, None, A, A), A, ws - 1) == WS
     assert run(p, t, nv.MoeLora(64, 1.0, A, A, None, None), A, ws - 1) == WS
     assert run(nv.MoeProblem(0, 8, 2, 256, 128, 0), t, lo, None, 0) == OK
+
+
+def _streamk_parts(M, N, K, wgs=256, tile=256):
+    """Most parts one 256 x 256 tile is cut into when wgs workgroups take the
+    tiles' K steps in order, workgroup w the steps [w S / wgs, (w + 1) S / wgs)
+    (brute force over the workgroups' ranges)."""
+    ks = K // 64
+    tiles = -(-M // tile) * -(-N // tile)
+    S = tiles * ks
+    parts = [0] * tiles
+    for w in range(wgs):
+        lo, hi = w * S // wgs, (w + 1) * S // wgs
+        for t in range(lo // ks, (hi - 1) // ks + 1):
+            parts[t] += 1
+    return max(parts)
+
+
+# Long rows on the 256 x 256 tile that take stream-K (the GPU parity cases and
+# o_proj at M = 1536, 3072, 4096): the W4A16 workspace is the fp32 parts,
+# [most parts per tile, M, N], 256-byte aligned.
+@pytest.mark.parametrize("M,N,K", [(1400, 6001, 4160), (1536, 5888, 4352), (1700, 5000, 16384),
+                                   (1024, 5632, 8192), (3000, 6000, 8320), (1536, 6144, 16384),
+                                   (3072, 6144, 16384), (4096, 6144, 16384)])
+def test_streamk_workspace_matches_partition(M, N, K):
+    L = nv.lib()
+    parts = _streamk_parts(M, N, K)
+    assert 2 <= parts <= 8
+    want = -(-(parts * M * N * 4) // 256) * 256
+    assert L.nvfp4_gemm_w4a16_workspace_size(M, N, K) == want
