@@ -199,14 +199,20 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, SAct am) {
         return p;
     }
     if (M > 64) {
-        // 65-128 rows (512-K stages): only on short rows with 64-row weight
-        // tiles and no K split (measured on MI355X: q_b_proj M = 96 / 128
-        // 30.6 / 23.6 -> 16.3 / 16.9 us; on o_proj, and with any K split, the
-        // tiles are as fast or faster)
-        if (!lds || !short_k || (N + 63) / 64 < 192) return p;
-        p.use = true;
-        p.nb = 4;
-        p.krange = krange_of(1);
+        // 65-128 rows (512-K stages), 64-row weight tiles, the fewest K splits
+        // (one or two) that give 192 workgroups (measured on MI355X: q_b_proj
+        // M = 96 / 128 unsplit 30.6 / 23.6 -> 16.3 / 16.9 us; o_proj 6144 x
+        // 16384, pre-packed activation, split 2: 50.4 / 52.0 -> 46.8 / 47.0 us,
+        // where split 1 took 77 us and splits 4 and 8 49-52 us)
+        if (!lds) return p;
+        for (int s = 1; s <= 2 && K / 128 >= s; ++s) {
+            if (((N + 63) / 64) * s < 192) continue;
+            p.use = true;
+            p.nb = 4;
+            p.ksplit = s;
+            p.krange = krange_of(s);
+            return p;
+        }
         return p;
     }
     if (lds) {

@@ -1,8 +1,9 @@
 """GPU parity of the weight-streaming small-batch GEMM (the planner sends
 W4A4, pre-packed W4A4 and W4A16 products with M <= 64 to it on short rows,
 W4A16 with M = 5..16 on long rows (bf16 activation streamed through LDS),
-pre-packed/one-call W4A4 with M = 65..128 on short rows (512-K ring stages,
-the waves split into four K units and two batch halves), and
+pre-packed/one-call W4A4 with M = 65..128 (512-K ring stages, the waves
+split into four K units and two batch halves; on long rows with K split in
+two), and
 pre-packed/one-call W4A4 with M = 5..64 on long rows) against the
 oracle, elementwise |y - ref| <= 1e-3 + 1e-2 |ref|, on sampled outputs of
 problems large enough for the planner to pick it (at least 192 workgroups).
@@ -29,7 +30,8 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(3, 12288, 2048), (17, 12288, 1152), (50, 12290, 640), (64, 12288, 4096), (8, 12288, 2048), (40, 6144, 16384),
           (5, 6144, 16384), (16, 3072, 32768), (33, 12352, 1024),
-          (65, 12288, 2048), (100, 12290, 1152), (128, 16384, 640), (97, 12352, 4096)]
+          (65, 12288, 2048), (100, 12290, 1152), (128, 16384, 640), (97, 12352, 4096),
+          (100, 6144, 8320), (128, 6160, 16384), (65, 6146, 4224)]
 
 
 def _sample(M, N, seed):
