@@ -7,9 +7,9 @@ q_b_proj (16384 x 2048); the W4A4 GEMM (from bf16 and from a pre-packed
 activation) and the W4A16 GEMM at M in {1, 8, ..., 4096} on both shapes; the routed-expert MoE layer (4096 tokens, 256 experts, top-8, hidden
 6144, intermediate 2048) in W4A16 and W4A4 mode, with and without a rank-64
 bf16 LoRA on its experts.  Inputs are resident in HBM
-before timing starts.  Weight-streaming kernels cycle through enough weight
-copies that every launch reads its weights from HBM, not from the 256 MB
-last-level cache.
+before timing starts.  GEMV and GEMM rows cycle through enough weight copies
+(10 of o_proj, 30 of q_b_proj: about 565 MB each) that every launch reads its
+weights from HBM, not from the 256 MB last-level cache.
 
 The headline value is the batch-1 o_proj GEMV's effective HBM bandwidth
 (packed codes + scale bytes per launch / mean launch time).  Per-kernel times
@@ -432,7 +432,7 @@ def main():
                 nv.quantize(x, global_scale=isc[:1])
                 y = torch.empty((M, N), dtype=torch.int16, device=dev)
                 ws = nv.workspace(nv.gemm_w4a4_workspace_size(M, N, K), dev)
-                use = cs if M <= 256 else cs[:2]
+                use = cs   # launches cycle through all copies across steps (more than the 256 MB cache)
                 calls = []
                 for c, s, g in use:
                     a = (P(x), P(isc), M, N, K, P(c), P(s), P(g), P(y), P(ws), ws.numel(), sptr)
