@@ -708,9 +708,9 @@ hipError_t launch_cfg(const GemmArgs& g0, int grid_m, hipStream_t stream) {
     } else if (g.sk_wgs > 0) {
         // stream-K: ungrouped partial sums with the per-step scale loads only
         // (the scale preload and the two-step stages assume one K range per
-        // workgroup)
+        // workgroup); built for the 256 x 256 tile, the one the plans use it on
         const int64_t steps = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN) * (g.K / 64);
-        if constexpr (EP == Epi::kPartialF32 && SJ == 0 && !K2) {
+        if constexpr (EP == Epi::kPartialF32 && SJ == 0 && !K2 && C::BM == 256 && C::BN == 256) {
             if (g.ksplit != 1 || g.sk_wgs > steps || g.sk_y == nullptr) return hipErrorInvalidValue;
             hipLaunchKernelGGL((k_gemm_a16<TM, TN, WM, WN, NS, AF, EP, WPE, SJ, K2, true>), dim3((unsigned)g.sk_wgs),
                                dim3(C::NT), 0, stream, g);
@@ -741,10 +741,6 @@ template <AFmt AF, Epi EP>
 hipError_t launch_tile(const GemmArgs& g, A16Tile tile, int grid_m, hipStream_t stream) {
     switch (tile) {
         case A16Tile::k256x256_w128x64: return launch_cfg<4, 2, 2, 4, 3, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x256_w128x128: return launch_cfg<4, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w128x64: return launch_cfg<4, 2, 2, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k256x128_w64x64: return launch_cfg<2, 2, 4, 2, 2, AF, EP>(g, grid_m, stream);
-        case A16Tile::k128x256_w64x128: return launch_cfg<2, 4, 2, 2, 2, AF, EP>(g, grid_m, stream);
         case A16Tile::k128x128_w64x64: return launch_cfg<2, 2, 2, 2, 2, AF, EP, 3>(g, grid_m, stream);
         case A16Tile::k128x128_w32x64: return launch_small<1, 2, 4, 2, 3, AF, EP>(g, grid_m, stream);
         case A16Tile::k64x256_w64x64: return launch_small<2, 2, 1, 4, 3, AF, EP>(g, grid_m, stream);
@@ -911,10 +907,6 @@ hipError_t launch_reduce_ks(const float* partial, int64_t total, const float* g0
 int a16_tile_rows(A16Tile t) {
     switch (t) {
         case A16Tile::k256x256_w128x64: return 256;
-        case A16Tile::k256x256_w128x128: return 256;
-        case A16Tile::k256x128_w128x64: return 256;
-        case A16Tile::k256x128_w64x64: return 256;
-        case A16Tile::k128x256_w64x128: return 128;
         case A16Tile::k128x128_w64x64: return 128;
         case A16Tile::k128x128_w32x64: return 128;
         case A16Tile::k64x256_w64x64: return 64;
@@ -927,10 +919,6 @@ int a16_tile_rows(A16Tile t) {
 int a16_tile_cols(A16Tile t) {
     switch (t) {
         case A16Tile::k256x256_w128x64: return 256;
-        case A16Tile::k256x256_w128x128: return 256;
-        case A16Tile::k256x128_w128x64: return 128;
-        case A16Tile::k256x128_w64x64: return 128;
-        case A16Tile::k128x256_w64x128: return 256;
         case A16Tile::k128x128_w64x64: return 128;
         case A16Tile::k128x128_w32x64: return 128;
         case A16Tile::k64x256_w64x64: return 256;

@@ -172,10 +172,6 @@ struct GemmArgs {
 // and the per-wave tile.
 enum class A16Tile : int {
     k256x256_w128x64 = 0,
-    k256x256_w128x128 = 1,
-    k256x128_w128x64 = 2,
-    k256x128_w64x64 = 3,
-    k128x256_w64x128 = 4,
     k128x128_w64x64 = 5,
     k128x128_w32x64 = 6,
     k64x256_w64x64 = 7,
