@@ -175,7 +175,8 @@ int32_t nvfp4_gemv_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
  * unless M <= 4 (or M <= 8 with K <= 4096 or K == 16384) the weight codes must span less
  * than 2 GiB (N * K / 2 < 2^31); else UNSUPPORTED.  Workspace: nvfp4_gemm_w4a4_workspace_size(M, N, K)
  * bytes (the quantized X, held as its exact products q * s in 16-bit form,
- * and, for small M, split-K partial sums).
+ * and the fp32 partial sums of a K split or, on long rows, of tiles whose K
+ * range several workgroups share).
  * ------------------------------------------------------------------------ */
 size_t nvfp4_gemm_w4a4_workspace_size(int64_t M, int64_t N, int64_t K);
 int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, int64_t N, int64_t K,
@@ -194,7 +195,8 @@ int32_t nvfp4_gemm_w4a4(const uint16_t* x, const float* input_scale, int64_t M, 
  * static scale the codes were made with); w_* as in the GEMV; y bf16 [M, N].
  * Same shape limits as nvfp4_gemm_w4a4.  Workspace:
  * nvfp4_gemm_w4a4_packed_workspace_size(M, N, K) bytes (the activation
- * expanded to its exact products q * s, and split-K partial sums).
+ * expanded to its exact products q * s, and fp32 partial sums as for
+ * nvfp4_gemm_w4a4).
  * ------------------------------------------------------------------------ */
 size_t nvfp4_gemm_w4a4_packed_workspace_size(int64_t M, int64_t N, int64_t K);
 int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global, int64_t M,
@@ -212,8 +214,9 @@ int32_t nvfp4_gemm_w4a4_packed(const uint8_t* a_codes, const uint8_t* a_scales, 
  * Small M runs the GEMV kernels; larger M runs MFMA tiles whose weight
  * operand is decoded to the exact bf16 values q * s.  K % 64 == 0, and when
  * the tiles run the weight codes must span less than 2 GiB; else UNSUPPORTED.
- * Workspace: nvfp4_gemm_w4a16_workspace_size(M, N, K) bytes (split-K partial
- * sums; 0 when none are needed, and then workspace may be NULL).
+ * Workspace: nvfp4_gemm_w4a16_workspace_size(M, N, K) bytes (fp32 partial
+ * sums as for nvfp4_gemm_w4a4; 0 when none are needed, and then workspace
+ * may be NULL).
  * ------------------------------------------------------------------------ */
 size_t nvfp4_gemm_w4a16_workspace_size(int64_t M, int64_t N, int64_t K);
 int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_codes,
