@@ -162,6 +162,10 @@ def test_gemm_stream_k(orc, M, N, K):
     isc = np.float32(orc.global_scale(x))
     y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
     y16 = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    # the pre-packed entry runs the same tiles on the same quantized operand
+    ac, asc, ag = nv.quantize(dev_bf16(x), static_scale=float(isc))
+    yp = host_bf16_f32(nv.gemm_w4a4_packed(ac, asc, ag, c, s, g))
+    np.testing.assert_array_equal(yp.view(np.uint32), y.view(np.uint32), err_msg="stream-K packed vs one-call")
     rng = np.random.default_rng(M + N + K)
     rows = np.unique(np.concatenate([np.minimum(M - 1, r0 + rng.choice(256, 6, replace=False))
                                      for r0 in range(0, M, 256)] + [[0, M - 1]]))
