@@ -27,6 +27,8 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+// static quantizes of at most this many blocks run four lanes per block
+constexpr int64_t kQuadMaxBlocks = (int64_t)1 << 20;
 
 // Pass 1: per-workgroup maximum of |x| as a bf16 magnitude pattern (for finite
 // values the pattern order is the value order).  Grid-stride over 16-byte
@@ -159,6 +161,42 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
     }
 }
 
+// Small static-scale inputs without a gather: four lanes per 16-element
+// block, each holding four consecutive elements (one 8-byte load, so a wave
+// reads 512 contiguous bytes).  The block maximum is a quad reduction, every
+// lane derives the block's scale from it (block_enc) and encodes its four
+// elements with encode_one: the same fp32 steps as encode_block.  A launch of
+// few blocks is bound by one thread's serial encode, which this cuts to a
+// quarter.  Lane q of block b writes code bytes 2q, 2q + 1 of the block (the
+// element order of encode_block), lane 0 the scale byte.
+__global__ __launch_bounds__(kThreads) void k_quantize_quad(PackArgs a) {
+    const float Sg = *a.sg_ptr;
+    if (a.global_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.global_out = Sg;
+    const float t = 6.0f * Sg;
+    const int64_t nquad = a.rows * (a.cols / 4);   // a multiple of 4: quads of a block are whole
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const bool ok = i < nquad;
+    const int64_t e = ok ? 4 * i : 0;
+    const uint2 v = *reinterpret_cast<const uint2*>(a.x + e);
+    uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+    m = max(m, dpp_u32<0xB1>(m));    // quad_perm [1,0,3,2]
+    m = max(m, dpp_u32<0x4E>(m));    // quad_perm [2,3,0,1]: the block maximum
+    const BlockEnc be = block_enc(m, Sg, t);
+    const uint32_t c = encode_one(v.x, be) | (encode_one(v.x >> 16, be) << 4) | (encode_one(v.y, be) << 8) |
+                       (encode_one(v.y >> 16, be) << 12);
+    if (!ok) return;
+    if (a.codes != nullptr) {
+        reinterpret_cast<uint16_t*>(a.codes)[i] = (uint16_t)c;
+        if ((i & 3) == 0) a.scales[i >> 2] = (uint8_t)be.s8;
+    }
+    if (a.xhat != nullptr) {
+        // q * s for the 4 elements, exact in f16 and bf16
+        const uint4 q = a.xhat_bf16 ? fp4x8_scaled_bf16_bits(c, be.s)
+                                    : __builtin_bit_cast(uint4, fp4x8_scaled_f16(c, (_Float16)be.s));
+        *reinterpret_cast<uint2*>(a.xhat + e) = make_uint2(q.x, q.y);
+    }
+}
+
 // Dequantize: one piece of 8 elements (4 code bytes, half a block) per
 // thread per step, two steps per iteration with both loads issued first.
 // Consecutive threads take consecutive pieces, so every load and every
@@ -281,6 +319,12 @@ hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, 
 
 hipError_t launch_quantize_pack(const PackArgs& a, hipStream_t stream) {
     const int64_t nblk = a.rows * (a.cols / 16);
+    if (a.mode == ScaleMode::kStatic && a.src_row == nullptr && a.rows_valid == nullptr && nblk > 0 &&
+        nblk <= kQuadMaxBlocks) {
+        hipLaunchKernelGGL(k_quantize_quad, dim3((unsigned)((4 * nblk + kThreads - 1) / kThreads)), dim3(kThreads),
+                           0, stream, a);
+        return hipGetLastError();
+    }
     // two blocks per thread per iteration; 4096 workgroups measured best on
     // MI355X for 65536 x 6144 (202 against 212 us with 8192 and one block)
     const int grid = grid_for(nblk, kThreads * 2, 4096);
