@@ -374,9 +374,12 @@ def _skewed_routing(counts, k, seed):
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_moe_rows_beyond_full_tiles(orc, mode):
-    """Experts with more rows than one 128-row tile: 150, 160, 161, 129, 261
-    (three tiles) and 39 rows, so partly filled tiles follow full ones."""
-    counts = [150, 160, 161, 129, 261, 39]
+    """Experts around the grouped GEMMs' 192-row tiles (four 96 x 64 waves; a
+    tile of at most 128 rows splits them 64 / 64): 150, 160, 161 and 129 rows
+    (one tile, the second wave row partly filled), 192 (one full tile), 193
+    and 261 (a second tile of 1 and 69 rows), 128 (the largest 64 / 64
+    split), 95, 64 and 39 rows (second wave row partly filled or empty)."""
+    counts = [150, 160, 161, 129, 261, 39, 192, 193, 128, 64, 95]
     k, H, I = 3, 256, 128
     ids, wts = _skewed_routing(counts, k, seed=9)
     assert np.array_equal(np.bincount(ids.ravel(), minlength=len(counts)), counts)
