@@ -409,3 +409,42 @@ def test_moe_many_experts_many_runs(orc):
     y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A16)
     torch.cuda.synchronize()
     assert_close(host_bf16_f32(y), ref, "moe many experts")
+
+
+def _random_gemm_shapes(n=12, seed=2027):
+    """Seeded (M, N, K) draws spread over the planner's regimes: batch rows
+    1-64 (GEMV, weight streaming), 65-256 (stream kernel or tiles with K
+    splits) and 257-3000 (256 x 256 tiles, split or stream-K), K a multiple
+    of 64 from 64 to 12288, N from 16 to 6200 (odd counts included)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        band = i % 3
+        M = int(rng.integers(1, 65) if band == 0 else rng.integers(65, 257) if band == 1 else rng.integers(257, 3001))
+        K = 64 * int(rng.integers(1, 193))
+        N = int(rng.integers(16, 6201))
+        while N * K > 40_000_000:         # keep the oracle's weight quantize to a few seconds
+            N //= 2
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_gemm_shapes())
+def test_gemm_random_shapes(orc, M, N, K):
+    print(f"random gemm M={M} N={N} K={K}", flush=True)
+    w = wl.layer_weight((N, K), seed=M + N + K)
+    x = wl.activations(M, K, seed=3 * M + K)
+    (c0, s0, g0), (c, s, g) = _quant_both(orc, w)
+    isc = np.float32(orc.global_scale(x))
+    y = host_bf16_f32(nv.gemm_w4a4(dev_bf16(x), torch.tensor([isc], device=device()), c, s, g))
+    y16 = host_bf16_f32(nv.gemm_w4a16(dev_bf16(x), c, s, g))
+    ac, asc, ag = nv.quantize(dev_bf16(x), static_scale=float(isc))
+    yp = host_bf16_f32(nv.gemm_w4a4_packed(ac, asc, ag, c, s, g))
+    np.testing.assert_array_equal(yp.view(np.uint32), y.view(np.uint32), err_msg="packed vs one-call")
+    rng = np.random.default_rng(M * N + K)
+    rows = np.unique(np.concatenate([rng.choice(M, min(M, 24), replace=False), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, min(N, 64), replace=False), [0, N - 1]]))
+    assert_close(y[np.ix_(rows, cols)], orc.gemm_w4a4(x[rows], isc, c0[cols], s0[cols], g0),
+                 f"random gemm {M}x{N}x{K}")
+    assert_close(y16[np.ix_(rows, cols)], orc.gemv_w4a16(x[rows], c0[cols], s0[cols], g0),
+                 f"random gemm w4a16 {M}x{N}x{K}")
