@@ -448,3 +448,35 @@ def test_gemm_random_shapes(orc, M, N, K):
                  f"random gemm {M}x{N}x{K}")
     assert_close(y16[np.ix_(rows, cols)], orc.gemv_w4a16(x[rows], c0[cols], s0[cols], g0),
                  f"random gemm w4a16 {M}x{N}x{K}")
+
+
+def _random_moe_shapes(n=6, seed=909):
+    """Seeded (T, E, k, H, I) draws: 1-400 tokens, 2-40 experts, top-1..8,
+    H and I multiples of 64 up to 512 and 320, so that experts hold from no
+    rows to a few hundred (one or two 192-row tiles, the 64 / 64 split)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(2, 41))
+        k = int(rng.integers(1, min(8, E) + 1))
+        out.append((int(rng.integers(1, 401)), E, k, 64 * int(rng.integers(1, 9)), 64 * int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("T,E,k,H,I", _random_moe_shapes())
+def test_moe_random_shapes(orc, T, E, k, H, I, mode):
+    print(f"random moe T={T} E={E} k={k} H={H} I={I} mode={mode}", flush=True)
+    x, ids, wts, cw, gw = _moe_case(orc, T, E, k, H, I, seed=T * 7 + E * 3 + k)
+    if mode == 0:
+        ref = orc.moe(x, ids, wts, *cw, mode=0)
+        y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A16)
+    else:
+        _, h = orc.moe(x, ids, wts, *cw, mode=0, want_h=True)
+        a13 = (orc.global_scale(x) * (1 + np.arange(E) / 32)).astype(np.float32)
+        a2 = (orc.global_scale(h) * (1 + np.arange(E) / 16)).astype(np.float32)
+        ref = orc.moe(x, ids, wts, *cw, mode=1, a13=a13, a2=a2)
+        y = nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A4,
+                                a13_scale=dev(a13), a2_scale=dev(a2))
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(y), ref, f"random moe T={T} E={E} k={k} H={H} I={I} mode={mode}")
