@@ -243,7 +243,9 @@ int32_t nvfp4_gemm_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, con
  * grouping, both grouped GEMMs and the combine run on the device with no
  * host round trip.  Workspace: nvfp4_moe_workspace_size(p) bytes (routing
  * tables, h, the fp32 per-slot outputs and, for mode 1, the quantized
- * activations held as their exact products q * s in f16).
+ * activations held as their exact products q * s in f16: one row per slot,
+ * or one per token when all E values of a13_scale are bitwise equal, which
+ * the device checks on every call; the output bits are the same either way).
  * ------------------------------------------------------------------------ */
 typedef struct nvfp4_moe_problem {
     int64_t T;      /* tokens */

@@ -389,7 +389,7 @@ constexpr int kMoeBM = 192;
 
 struct MoeLayout {
     size_t row_off = 0, tile_off = 0, perm = 0, inv = 0, pos_group = 0, route = 0;
-    size_t xq = 0, hq = 0, h = 0, y = 0, z13 = 0, z2 = 0, total = 0;
+    size_t xq = 0, hq = 0, h = 0, y = 0, z13 = 0, z2 = 0, shared = 0, total = 0;
 };
 
 // lora_rank > 0 adds the bf16 rank-r projections z13 [T, r] and z2 [S, r].
@@ -405,8 +405,10 @@ MoeLayout layout_moe(const nvfp4_moe_problem& p, int64_t lora_rank = 0) {
     l.route = off; off += align_up(moe_route_scratch_bytes((int64_t)S, (int32_t)p.E));
     if (p.mode == 1) {
         // the quantized activations as exact f16 products q * s, slot order
+        // (token order when every expert shares one a13 value), and that choice
         l.xq = off; off += align_up(S * (size_t)p.H * 2);
         l.hq = off; off += align_up(S * (size_t)p.I * 2);
+        l.shared = off; off += align_up(4);
     }
     l.h = off; off += align_up(S * (size_t)p.I * 2);
     l.y = off; off += align_up(S * (size_t)p.H * 4);
@@ -861,7 +863,13 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
 
     // GEMM 1: [g | u] = x^ W13^T, h = bf16(silu(g) * u).  W4A16 multiplies the
     // bf16 tokens (gathered by slot); W4A4 first quantizes them per expert
-    // group under a13_scale into their exact f16 products q * s.
+    // group under a13_scale into their exact f16 products q * s, one row per
+    // slot, or, when all E values of a13_scale are bitwise equal (the serving
+    // form with one input scale for the experts' gate/up projections), one
+    // row per token, which GEMM 1 then gathers by slot like the bf16 tokens:
+    // the same operand values from an eighth of the quantize work (the
+    // quantize pass takes that choice on the device and leaves it in the
+    // workspace for GEMM 1).
     const A16Tile tile = A16Tile::k192x128_w96x64;  // kMoeBM-row tiles, as the routing counted
     GemmArgs g1;
     g1.b_codes = t->w13_codes;
@@ -897,10 +905,17 @@ int32_t nvfp4_moe_grouped_gemm_lora(const nvfp4_moe_problem* p, const nvfp4_moe_
         a.sg_group = t->a13_scale;
         a.row_group = pos_group;
         a.xhat = xq;
+        int32_t* shared = at<int32_t>(workspace, l.shared);
+        a.n_groups = E;
+        a.shared_rows = p->T;
+        a.shared_out = shared;
         st = hip_status(launch_quantize_pack(a, s), "moe activation quantize");
         if (st) return st;
         g1.a = xq;
         g1.a_src_rows = S;
+        g1.a_rows = perm;
+        g1.a_div = (int32_t)p->top_k;
+        g1.a_rows_on = shared;
         g1.a_global = t->a13_scale;
         af = AFmt::kF16;
     } else {

@@ -338,6 +338,7 @@ void k_gemm_a16(GemmArgs g) {
     // ---- this lane's copy assignments (fixed for the whole K loop)
     // A slab sl = A_PER_W wave + u: rows 8 sl + lane / 8, LDS slot lane % 8,
     // which receives the row's 16-byte chunk slot ^ ((row / 2) % 8).
+    const bool a_gather = g.a_rows != nullptr && (g.a_rows_on == nullptr || *g.a_rows_on != 0);
     uint32_t va[C::A_PER_W];
 #pragma unroll
     for (int u = 0; u < C::A_PER_W; ++u) {
@@ -346,7 +347,7 @@ void k_gemm_a16(GemmArgs g) {
         const int64_t row = row_beg + r;
         uint32_t v = kOob;
         if (row < row_end) {
-            const int64_t src = g.a_rows ? (int64_t)(g.a_rows[row] / g.a_div) : row;
+            const int64_t src = a_gather ? (int64_t)(g.a_rows[row] / g.a_div) : row;
             v = (uint32_t)(src * KA) + 16u * cc;
         }
         va[u] = v;

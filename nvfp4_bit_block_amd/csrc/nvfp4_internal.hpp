@@ -42,6 +42,14 @@ struct PackArgs {
     // element (no global scale), as f16 or bf16 (both represent them exactly).
     uint16_t* xhat = nullptr;
     bool xhat_bf16 = false;
+    // kGrouped with n_groups > 0: when the n_groups scales sg_group[0 ..
+    // n_groups) are all bitwise equal, rows 0 .. shared_rows - 1 of x are
+    // quantized instead, ungathered, under sg_group[0] (output row r from
+    // source row r); every workgroup takes the same choice and workgroup 0
+    // stores it in *shared_out (1 shared, 0 per-row scales).
+    int32_t n_groups = 0;
+    int64_t shared_rows = 0;
+    int32_t* shared_out = nullptr;
 };
 
 hipError_t launch_amax_partial(const uint16_t* x, int64_t n, uint32_t* partial, int grid,
@@ -119,8 +127,9 @@ enum class Epi : int {
 struct GemmArgs {
     // A operand: 16-bit [*, K] rows (optionally gathered).
     const void* a = nullptr;
-    const int32_t* a_rows = nullptr;  // bf16 gather: A row of output row r = a_rows[r] / a_div
+    const int32_t* a_rows = nullptr;  // gather: A row of output row r = a_rows[r] / a_div
     int32_t a_div = 1;
+    const int32_t* a_rows_on = nullptr;  // optional device flag: the gather applies only when it is nonzero
     int64_t a_src_rows = 0;           // bf16 A: rows of the source tensor
     const float* a_global = nullptr;  // per group (or [1]); null = 1
     // B operand: NVFP4 [N, K] per group

@@ -104,14 +104,29 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
     if constexpr (MODE != ScaleMode::kGrouped) {
         if (a.global_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.global_out = Sg;
     }
+    // Grouped scales that are all one value: quantize the ungathered source
+    // rows once each (see PackArgs::n_groups).
+    bool shared = false;
+    if constexpr (MODE == ScaleMode::kGrouped) {
+        if (a.n_groups > 0) {
+            const uint32_t s0 = __float_as_uint(a.sg_group[0]);
+            bool eq = true;
+            for (int e = threadIdx.x; e < a.n_groups; e += kThreads) eq = eq && __float_as_uint(a.sg_group[e]) == s0;
+            shared = __syncthreads_and(eq ? 1 : 0) != 0;
+            if (blockIdx.x == 0 && threadIdx.x == 0) *a.shared_out = shared ? 1 : 0;
+            if (shared) Sg = a.sg_group[0];
+        }
+    }
     float t = 6.0f * Sg;
     const int64_t bpr = a.cols / 16;
-    const int64_t nblk = a.rows * bpr;
-    const int64_t rows_valid = a.rows_valid ? (int64_t)*a.rows_valid : a.rows;
+    const int64_t rows_valid =
+        shared ? min(a.shared_rows, a.rows) : (a.rows_valid ? (int64_t)*a.rows_valid : a.rows);
+    // blocks of the valid rows
+    const int64_t nblk = min(a.rows, max(rows_valid, (int64_t)0)) * bpr;
     // Two blocks per thread per iteration (b and b + stride), both loads issued
-    // before either block is encoded.  A slot past the end, or on a row at or
-    // beyond rows_valid (whose gather index may be unset), loads block 0 of
-    // source row 0 instead and stores nothing.
+    // before either block is encoded.  A slot past the end loads block 0 of
+    // source row 0 instead and stores nothing; rows at or beyond rows_valid
+    // (whose gather index may be unset) are never visited.
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t b0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; b0 < nblk; b0 += 2 * stride) {
         uint4 v[2][2];
@@ -121,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
         for (int p = 0; p < 2; ++p) {
             const int64_t b = b0 + p * stride;
             const int64_t r = (b < nblk ? b : b0) / bpr;
-            ok[p] = b < nblk && r < rows_valid;
+            ok[p] = b < nblk;
             rr[p] = r;
             cbb[p] = (b < nblk ? b : b0) - r * bpr;
-            const int64_t sr = !ok[p] ? 0 : (a.src_row ? (int64_t)(a.src_row[r] / a.src_div) : r);
+            const int64_t sr = !ok[p] ? 0 : (!shared && a.src_row ? (int64_t)(a.src_row[r] / a.src_div) : r);
             const uint4* src = reinterpret_cast<const uint4*>(a.x + sr * a.cols + (ok[p] ? cbb[p] * 16 : 0));
             v[p][0] = load_nt16(src);
             v[p][1] = load_nt16(src + 1);
@@ -134,8 +149,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(PackArgs a) {
             if (!ok[p]) continue;
             const int64_t b = b0 + p * stride, r = rr[p], cb = cbb[p];
             if constexpr (MODE == ScaleMode::kGrouped) {
-                Sg = a.sg_group[a.row_group[r]];
-                t = 6.0f * Sg;
+                if (!shared) {
+                    Sg = a.sg_group[a.row_group[r]];
+                    t = 6.0f * Sg;
+                }
             }
             uint32_t w[8] = {v[p][0].x, v[p][0].y, v[p][0].z, v[p][0].w,
                              v[p][1].x, v[p][1].y, v[p][1].z, v[p][1].w};

@@ -400,6 +400,31 @@ def test_moe_rows_beyond_full_tiles(orc, mode):
     assert_close(host_bf16_f32(y), ref, f"moe skewed routing mode {mode}")
 
 
+def test_moe_w4a4_shared_input_scale(orc):
+    """W4A4 with one a13 value for every expert quantizes each token once and
+    gathers it by slot; with one value differing on an expert that receives
+    no slot the layer quantizes per slot instead.  Both must give the same
+    bits, and the oracle's result."""
+    counts = [40, 90, 130, 0, 70, 150, 11, 109]
+    k, H, I = 4, 256, 128
+    ids, wts = _skewed_routing(counts, k, seed=21)
+    T, E = ids.shape[0], len(counts)
+    x, _, _, cw, gw = _moe_case(orc, 1, E, 1, H, I, seed=41)
+    x = wl.activations(T, H, seed=42)
+    _, h = orc.moe(x, ids, wts, *cw, mode=0, want_h=True)
+    a13 = np.full(E, orc.global_scale(x), np.float32)
+    a2 = np.full(E, orc.global_scale(h), np.float32)
+    ref = orc.moe(x, ids, wts, *cw, mode=1, a13=a13, a2=a2)
+    odd = a13.copy()
+    odd[3] *= 2.0
+    ys = [nv.moe_grouped_gemm(dev_bf16(x), dev(ids), dev(wts), *gw, mode=nv.MODE_W4A4,
+                              a13_scale=dev(sc), a2_scale=dev(a2)) for sc in (a13, odd, a13)]
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f32(ys[0]), ref, "moe w4a4 shared a13")
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    assert torch.equal(ys[0].view(torch.int16), ys[2].view(torch.int16))
+
+
 def test_moe_many_experts_many_runs(orc):
     """Routing over several workgroup runs of slots (2400 slots) and more
     experts than the scan has threads (1100), most experts with a few rows."""
