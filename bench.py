@@ -486,7 +486,9 @@ def main():
         wts_d = torch.from_numpy(wts).to(dev)
         out = torch.empty((T, H), dtype=torch.int16, device=dev)
         # static input scales, one per expert: a13 = amax(X)/(6*448) from the
-        # library's dynamic quantize of X; a2 is a generous analytic estimate
+        # library's dynamic quantize of X, the same value for every expert (the
+        # serving form, with the activation quantized once before routing: the
+        # layer then quantizes each token once); a2 is a generous analytic estimate
         # for h = silu(g)*u with g, u ~ N(0, s2), s2 = H * 0.02^2 * E[x^2]:
         # |h| stays below s2 * ln(#h) with margin, doubled (the pages' static
         # input_scale is likewise a generous per-tensor heuristic).

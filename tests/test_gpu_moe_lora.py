@@ -110,16 +110,21 @@ def full_moe():
     return dict(T=T, E=E, k=k, H=H, I=I, ids=ids, wts=wts, x=x, w13=w13, w2=w2, lora=lo)
 
 
-@pytest.mark.parametrize("mode,adapter", [(0, False), (1, False), (0, True), (1, True)])
-def test_moe_full_size_sampled_tokens(orc, full_moe, mode, adapter):
+@pytest.mark.parametrize("mode,adapter,shared", [(0, False, True), (1, False, True), (1, False, False),
+                                                 (0, True, True), (1, True, True)])
+def test_moe_full_size_sampled_tokens(orc, full_moe, mode, adapter, shared):
     """The GPU runs the whole layer in the benchmark's launch configuration;
     the oracle recomputes 6 sampled tokens (the first, the last and 4 drawn)
     from the experts they use (a token's output depends only on its own
-    routing and the expert weights)."""
+    routing and the expert weights).  W4A4 runs with one gate/up input scale
+    for all experts (tokens quantized once each) and with one per expert
+    (one quantized row per slot)."""
     f = full_moe
     T, E, H, I = f["T"], f["E"], f["H"], f["I"]
-    print(f"moe full size mode={mode} lora={adapter}", flush=True)
+    print(f"moe full size mode={mode} lora={adapter} shared_a13={shared}", flush=True)
     a13 = np.full(E, orc.global_scale(f["x"]) * 1.5, np.float32)
+    if not shared:
+        a13 = (a13 * (1 + np.arange(E) / 512)).astype(np.float32)
     a2 = np.full(E, 0.02, np.float32)
     scale = 1.0
     gkw = dict(a13_scale=dev(a13), a2_scale=dev(a2)) if mode == 1 else {}
@@ -138,7 +143,7 @@ def test_moe_full_size_sampled_tokens(orc, full_moe, mode, adapter):
         lora = {"scale": scale, "a13": lo["a13"], "b13": lo["b13"][used], "a2": lo["a2"], "b2": lo["b2"][used]}
     kw = dict(a13=a13[used], a2=a2[used]) if mode == 1 else {}
     ref = orc.moe(f["x"][rows], ids_s, f["wts"][rows], *host, mode=mode, lora=lora, **kw)
-    assert_close(host_bf16_f32(y)[rows], ref, f"moe full size mode={mode} lora={adapter}")
+    assert_close(host_bf16_f32(y)[rows], ref, f"moe full size mode={mode} lora={adapter} shared_a13={shared}")
 
 
 @pytest.mark.parametrize("mode", [0, 1])
