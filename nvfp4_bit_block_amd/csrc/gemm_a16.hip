@@ -622,6 +622,10 @@ void k_gemm_a16(GemmArgs g) {
     for (int u = 0; u + 1 < NS; ++u)
         if (nmain + u < nsteps) step(nmain + u, u);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // (the last steps' clamped re-reads may still be landing in the stage
+    // buffers of other waves: the bf16 epilogue below reuses them only after
+    // every wave has seen its own loads complete)
+    if constexpr (EP == Epi::kStoreBf16 || EP == Epi::kPartialF32) __syncthreads();
 
     // ---- epilogue: lane holds rows 8 (r/4) + 4 hf + r%4 of each 32x32 block, column c32.
     // Gate/up with out_q also quantizes h to NVFP4 under q_global[group]:
@@ -629,6 +633,48 @@ void k_gemm_a16(GemmArgs g) {
     // columns of one block of one row, so the block maximum is a 16-lane
     // reduction, and each lane encodes its own element with the quantizer's
     // rule (nvfp4_encode.hpp) and stores the exact product q * s as f16.
+    // Whole bf16 tiles leave through LDS: each wave writes a 32-row slab of
+    // its results there (the K loop ended on a barrier, so the stage buffers
+    // are free) and reads it back as 16-byte pieces of rows, so that a store
+    // instruction covers eight whole 128-byte row segments instead of two
+    // half segments of 2-byte elements.  Ragged edges and row strides that
+    // are not a multiple of 8 store element by element.
+    constexpr bool kBf16Tile = EP == Epi::kStoreBf16 || EP == Epi::kPartialF32;
+    constexpr int kSlab = TN * 64;   // bytes per row of a wave's 32-row slab
+    static_assert(!kBf16Tile || C::NW * 32 * kSlab <= NS * STG, "epilogue slabs");
+    if (kBf16Tile && (EP == Epi::kStoreBf16 || sk_whole)) {
+        uint16_t* const yb = EP == Epi::kStoreBf16 ? reinterpret_cast<uint16_t*>(g.out) : g.sk_y;
+        uint8_t* const slab = smem + wave * 32 * kSlab;
+        const bool vec = (g.ldo & 7) == 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = 8 * (r >> 2) + 4 * hf + (r & 3);
+                    *reinterpret_cast<uint16_t*>(slab + rr * kSlab + (32 * j + c32) * 2) =
+                        (uint16_t)f32_to_bf16_rne(acc[i][j][r] * sc);
+                }
+#pragma unroll 1
+            for (int p = 0; p < 32 * kSlab / 1024; ++p) {
+                const int e = 64 * p + lane, rr = e / (kSlab / 16), ch = e % (kSlab / 16);
+                const uint4 v = *reinterpret_cast<const uint4*>(slab + rr * kSlab + 16 * ch);
+                const int64_t row = row_beg + wrow + 32 * i + rr;
+                const int64_t col = (int64_t)tn * BN + wn * WTN + 8 * ch;
+                if (row >= row_end || col >= g.N) continue;
+                uint16_t* const dst = yb + row * g.ldo + col;
+                if (vec && col + 8 <= g.N) {
+                    *reinterpret_cast<uint4*>(dst) = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (col + q < g.N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+                }
+            }
+        }
+    } else {
     float sgq = 0.0f;
     if constexpr (kGateUp) {
         if (g.out_q) sgq = g.q_global[gi];
@@ -682,13 +728,15 @@ void k_gemm_a16(GemmArgs g) {
             }
         }
     }
+    }
     // next stream-K segment (the K loop ended on a barrier, so the stage
-    // buffers are free; the epilogue used registers only)
+    // buffers are free once every wave has left its epilogue)
     if constexpr (!SK) {
         break;
     } else {
         sk0 += seg_steps;
         if (sk0 >= sk1) break;
+        __syncthreads();   // the epilogue slabs share LDS with the next segment's stages
     }
     }
 }
